@@ -1,0 +1,240 @@
+"""MoE-layer throughput on one MI355X.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload mixtral_8x7b] [--dist ...]
+
+One step = one pass of the whole single-GPU layer over one batch of seeded
+synthetic input already resident in HBM:
+
+    moe_route -> moe_layout -> moe_permute -> moe_grouped_gate_up -> moe_grouped_down -> moe_combine
+
+Prints ONE JSON line (everything else goes to stderr):
+  value       tokens/s of the layer (for an EP share: the share's own tokens per
+              rank, T/ep, per step)
+  roofline    the dominant kernel's algorithmic FLOP/s (or bytes/s) per launch over
+              its average launch time, measured with HIP events on the stream the
+              library launches on, against the MI355X datasheet peak
+  stages      the same per stage
+  cpu_baseline the CPU oracle timed on a bounded sample of the same workload
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
+PEAK_BF16_TFLOPS = 2516.6  # dense bf16 MFMA: 256 CU x 4096 flop/clk x 2.4 GHz (the 2.5 PF figure)
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mixtral_8x7b")
+    ap.add_argument("--dist", default=None)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0,
+                    help="seconds of oracle work for the CPU baseline sample")
+    return ap.parse_args()
+
+
+def traffic_record(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was
+    taken on the current kernel source (else None)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_counters.md")
+    src = os.path.join(ROOT, "combine_top_router_amd", "csrc", "grouped_gemm.hip")
+    if not os.path.exists(path):
+        return None
+    rec = {}
+    for line in open(path):
+        if line.startswith("- ") and ":" in line:
+            k, v = line[2:].split(":", 1)
+            rec[k.strip()] = v.strip().strip("`")
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    if rec.get("source_sha256_16") != sha or "hbm_bytes_per_launch" not in rec:
+        return None
+    return float(rec["hbm_bytes_per_launch"])
+
+
+def cpu_baseline(cfg, dist, layer_args, budget_s):
+    """The oracle, as it stands, on the first S tokens of the same workload."""
+    import numpy as np
+    import torch
+    import threadpoolctl
+
+    from oracle import bf16 as obf16, layer as olayer, route as oroute
+
+    x, logits, w1, w3, w2, share = layer_args
+    ep = cfg.ep_size
+    dec = lambda t: obf16.decode(t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16))  # noqa: E731
+    logits_np = logits.cpu().numpy()
+    first = cfg.local_experts(share)[0]
+    cache = {}
+
+    def weights_for(tokens):
+        idx, _ = oroute.route(logits_np[:tokens], cfg.top_k)
+        need = sorted({int(e) - first for e in np.unique(idx)
+                       if 0 <= int(e) - first < len(cfg.local_experts(share))})
+        for e in need:
+            if e not in cache:
+                cache[e] = (dec(w1[e]), dec(w3[e]), dec(w2[e]))
+        return need
+
+    def run(tokens):
+        weights_for(tokens)  # decoding the bf16 weights is not oracle work: untimed
+        xs = dec(x[:tokens])
+        t0 = time.perf_counter()
+        olayer.layer(xs, logits_np[:tokens], cfg.top_k, lambda e: cache[e], cfg.num_experts,
+                     ep, share, cfg.align)
+        return time.perf_counter() - t0
+
+    per_expert_bytes = 3 * cfg.hidden * cfg.inter * 8
+    max_experts = max(1, int(48e9 // per_expert_bytes))
+    s = ep * max(1, 32 // ep)
+    t = run(s)
+    while t < budget_s / 8 and s < cfg.num_tokens:
+        s = min(cfg.num_tokens, s * 4)
+        if len(weights_for(s)) > max_experts:
+            s //= 4
+            break
+        t = run(s)
+    target = int(s * budget_s / max(t, 1e-3)) // ep * ep
+    target = max(ep, min(cfg.num_tokens, target))
+    while target > s and len(weights_for(target)) > max_experts:
+        target = max(s, target // 2 // ep * ep)
+    if target != s:
+        s, t = target, run(target)
+    info = threadpoolctl.threadpool_info()
+    threads = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
+    per_rank = s // ep
+    return {"value": per_rank / t, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": (f"first {s} of {cfg.num_tokens} tokens ({per_rank} per rank), whole oracle "
+                       f"layer (route, layout, permute, fp64 SwiGLU experts, fp64 combine), "
+                       f"{t:.1f} s, numpy BLAS threads {threads}, "
+                       f"{len(os.sched_getaffinity(0))} host cores visible")}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs one GPU only (got --gpus {args.gpus}): this build measures one "
+              "GPU's share of the layer; sharding across GPUs is not implemented.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import combine_top_router_amd as moe
+    import workloads
+
+    cfg = workloads.get(args.workload)
+    dist = args.dist or cfg.dists[0]
+    share = cfg.local_rank
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"workload {cfg.name} dist {dist} share {share}: generating inputs")
+    x, logits = workloads.gen.routing_inputs(cfg, dist, args.seed, device=dev)
+    w1, w3, w2 = workloads.gen.expert_weights(cfg, cfg.local_experts(share), args.seed, device=dev)
+    layer = moe.MoELayer(cfg.num_tokens, cfg.hidden, cfg.num_experts, cfg.top_k, cfg.inter,
+                         w1, w3, w2, cfg.ep_size, share, cfg.align)
+    stages = layer.stages(x, logits)
+    stream = torch.cuda.current_stream(dev)
+
+    for _ in range(args.warmup):
+        for _, run in stages:
+            run()
+    torch.cuda.synchronize()
+
+    # algorithmic work of this batch (read once, outside the timed region)
+    counts = layer.L.local_counts.cpu().numpy().astype(np.int64)
+    dst = layer.L.dst_row.cpu().numpy()
+    n_loc = int(counts.sum())
+    t_loc = int((dst >= 0).any(axis=1).sum())
+    e_act = int((counts > 0).sum())
+    T, H, I, E, k = cfg.num_tokens, cfg.hidden, cfg.inter, cfg.num_experts, cfg.top_k
+    N = T * k
+    work = {
+        "route": ("hbm", T * E * 4 + N * 8),
+        "layout": ("hbm", N * 4 * 2 + n_loc * 4),
+        "permute": ("hbm", (t_loc + n_loc) * H * 2),
+        "gate_up": ("mfma", 4.0 * n_loc * H * I),
+        "down": ("mfma", 2.0 * n_loc * H * I),
+        "combine": ("hbm", n_loc * H * 2 + N * 8 + T * H * 2),
+    }
+
+    n_st = len(stages)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_st + 1)]
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        evs[s][0].record(stream)
+        for i, (_, run) in enumerate(stages):
+            run()
+            evs[s][i + 1].record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    stage_ms = {name: float(np.mean([evs[s][i].elapsed_time(evs[s][i + 1])
+                                     for s in range(args.steps)]))
+                for i, (name, _) in enumerate(stages)}
+    step_ms = elapsed / args.steps * 1e3
+    tokens_per_step = T // cfg.ep_size
+    value = tokens_per_step * args.steps / elapsed
+
+    stage_out = {}
+    for name, ms in stage_ms.items():
+        bound, amount = work[name]
+        if bound == "hbm":
+            ach = amount / (ms * 1e-3) / 1e9
+            stage_out[name] = {"ms": round(ms, 4), "bound": "hbm", "GB/s": round(ach, 1),
+                               "frac": round(ach / PEAK_HBM_GBS, 4), "bytes": int(amount)}
+        else:
+            ach = amount / (ms * 1e-3) / 1e12
+            stage_out[name] = {"ms": round(ms, 4), "bound": "mfma", "TFLOP/s": round(ach, 1),
+                               "frac": round(ach / PEAK_BF16_TFLOPS, 4), "flops": amount}
+    dom = max(stage_ms, key=stage_ms.get)
+    d = stage_out[dom]
+    traffic = traffic_record(dom, cfg.name) if d["bound"] == "mfma" else None
+    if d["bound"] == "mfma":
+        roof = {"bound": "mfma", "kernel": dom, "achieved": d["TFLOP/s"],
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": d["frac"],
+                "traffic": traffic}
+    else:
+        roof = {"bound": "hbm", "kernel": dom, "achieved": d["GB/s"], "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": d["frac"], "traffic": traffic}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample")
+        cpu = cpu_baseline(cfg, dist, (x, logits, w1, w3, w2, share), args.cpu_budget)
+
+    rec = {
+        "metric": "MoE layer tokens/s on 1 MI355X; % HBM roofline (perm/combine), % MFMA (GEMM)",
+        "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(step_ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": cfg.name, "tokens": T, "hidden": H, "experts": E,
+                   "local_experts": len(cfg.local_experts(share)), "top_k": k, "inter": I,
+                   "ep_size": cfg.ep_size, "local_rank": share, "align": cfg.align,
+                   "routing": dist, "local_rows": n_loc, "seed": args.seed},
+        "roofline": roof, "stages": stage_out, "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

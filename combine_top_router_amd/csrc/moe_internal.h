@@ -1,0 +1,99 @@
+// Internal helpers shared by the HIP kernels of libmoe (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kWave = 64;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // 16 bytes = 8 bf16
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// bf16 bits -> fp32 (exact).
+__device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
+
+// Two fp32 -> two bf16 (round to nearest even, v_cvt_pk_bf16_f32), packed lo|hi.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2 v;
+  v[0] = static_cast<__bf16>(lo);
+  v[1] = static_cast<__bf16>(hi);
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ uint16_t to_bf16(float f) {
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+
+// Eight bf16 in a 16-byte vector -> fp32.
+__device__ __forceinline__ void unpack8(const u32x4& v, float (&f)[8]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = bf16_lo(v[i]);
+    f[2 * i + 1] = bf16_hi(v[i]);
+  }
+}
+
+__device__ __forceinline__ u32x4 pack8(const float (&f)[8]) {
+  u32x4 v;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = pack_bf16x2(f[2 * i], f[2 * i + 1]);
+  return v;
+}
+
+// A value every lane of the wave agrees on, moved to a scalar register.
+__device__ __forceinline__ int64_t uniform(int64_t v) {
+  uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(static_cast<uint64_t>(v) >> 32));
+  return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+}  // namespace moe
+
+// ---------------------------------------------------------------------------
+// Host-side launchers, one per kernel family (defined in the .hip files).
+// They assume arguments were checked by the C ABI layer.
+namespace moe {
+
+hipError_t launch_route(const float* logits, int64_t T, int E, int k, int32_t* idx, float* w,
+                        hipStream_t s);
+
+struct LayoutPlan {
+  int64_t T;
+  int E, k, ep, first, e_loc, align;
+  int64_t chunk;      // assignments per source rank, (T/ep)*k
+  int tile;           // assignments per tile (multiple of 256)
+  int tiles_per_rank;
+  int num_tiles;
+  int key_bits;       // ballot rounds to tell local experts (and "not local") apart
+};
+LayoutPlan make_layout_plan(int64_t T, int E, int k, int ep, int local_rank, int align);
+size_t layout_workspace_bytes(const LayoutPlan& p);
+hipError_t launch_layout(const LayoutPlan& p, const int32_t* topk_idx, int32_t* expert_counts,
+                         int32_t* send_counts, int32_t* split_matrix, int32_t* recv_counts,
+                         int32_t* output_splits, int32_t* offsets, int32_t* dst_row,
+                         int32_t* src_row, int64_t m_cap, void* ws, hipStream_t s);
+
+hipError_t launch_permute(const void* x, int64_t T, int H, int k, const int32_t* dst_row,
+                          int64_t m_cap, void* x_perm, hipStream_t s);
+hipError_t launch_combine(const void* y, int64_t y_rows, const int32_t* dst_row, const float* w,
+                          int64_t T, int H, int k, void* out, hipStream_t s);
+hipError_t launch_pack(const void* w, int64_t mats, int rows, int cols, void* wt, hipStream_t s);
+
+hipError_t launch_gate_up(const void* x_perm, const int32_t* offsets, const int32_t* counts,
+                          int e_loc, int64_t m_cap, int H, int I, const void* w1t,
+                          const void* w3t, void* h, hipStream_t s);
+hipError_t launch_down(const void* h, const int32_t* offsets, const int32_t* counts, int e_loc,
+                       int64_t m_cap, int I, int H, const void* w2t, void* y, hipStream_t s);
+
+int device_cu_count();
+
+}  // namespace moe

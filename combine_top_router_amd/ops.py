@@ -1,0 +1,231 @@
+"""Thin PyTorch binding of libmoe: argument marshalling only.
+
+PyTorch supplies device memory and the current HIP stream; every step of
+the path runs in the library's HIP kernels. Each function checks that its
+tensors live on the GPU with the dtype and layout the C ABI expects, hands
+raw pointers to the library, and raises ``MoEError`` on a non-OK status.
+"""
+from __future__ import annotations
+
+import ctypes as C
+from dataclasses import dataclass
+
+import torch
+
+from ._lib import LayoutDesc, MoEError, check, lib
+
+
+def _stream(dev: torch.device):
+    return C.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _ptr(t):
+    return C.c_void_p(t.data_ptr()) if t is not None else C.c_void_p(0)
+
+
+def _need(t: torch.Tensor, name: str, dtype, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU (got {t.device})")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
+
+
+def _empty(shape, dtype, dev):
+    return torch.empty(shape, dtype=dtype, device=dev)
+
+
+# ---------------------------------------------------------------- route
+
+def route(logits: torch.Tensor, top_k: int, topk_idx=None, topk_w=None):
+    """(topk_idx [T, k] int32, topk_w [T, k] float32) from logits [T, E] fp32."""
+    _need(logits, "logits", torch.float32)
+    T, E = logits.shape
+    dev = logits.device
+    topk_idx = _empty((T, top_k), torch.int32, dev) if topk_idx is None else topk_idx
+    topk_w = _empty((T, top_k), torch.float32, dev) if topk_w is None else topk_w
+    _need(topk_idx, "topk_idx", torch.int32, (T, top_k))
+    _need(topk_w, "topk_w", torch.float32, (T, top_k))
+    check("moe_route", lib().moe_route(_ptr(logits), T, E, top_k, _ptr(topk_idx), _ptr(topk_w),
+                                       _stream(dev)))
+    return topk_idx, topk_w
+
+
+# ---------------------------------------------------------------- layout
+
+def layout_desc(num_tokens, num_experts, top_k, ep_size=1, local_rank=-1, align=128) -> LayoutDesc:
+    return LayoutDesc(num_tokens, num_experts, top_k, ep_size, local_rank, align)
+
+
+def layout_m_cap(desc: LayoutDesc) -> int:
+    m = lib().moe_layout_m_cap(C.byref(desc))
+    if m < 0:
+        raise MoEError("moe_layout_m_cap", 1, "invalid layout descriptor")
+    return int(m)
+
+
+def layout_workspace_bytes(desc: LayoutDesc) -> int:
+    return int(lib().moe_layout_workspace_bytes(C.byref(desc)))
+
+
+@dataclass
+class Layout:
+    desc: LayoutDesc
+    m_cap: int
+    first_local: int
+    num_local: int
+    expert_counts: torch.Tensor  # [E]
+    send_counts: torch.Tensor    # [ep, E]
+    split_matrix: torch.Tensor   # [ep, ep]
+    recv_counts: torch.Tensor    # [ep, E_loc]
+    output_splits: torch.Tensor  # [ep]
+    offsets: torch.Tensor        # [E_loc + 1]
+    dst_row: torch.Tensor        # [T, k]
+    src_row: torch.Tensor        # [m_cap]
+    workspace: torch.Tensor      # bytes
+
+    @property
+    def local_counts(self) -> torch.Tensor:
+        return self.expert_counts[self.first_local:self.first_local + self.num_local]
+
+
+def alloc_layout(desc: LayoutDesc, device, m_cap=None) -> Layout:
+    T, E, k, ep = desc.num_tokens, desc.num_experts, desc.top_k, desc.ep_size
+    first = 0 if desc.local_rank < 0 else desc.local_rank * (E // ep)
+    el = E if desc.local_rank < 0 else E // ep
+    m_cap = layout_m_cap(desc) if m_cap is None else m_cap
+    i32 = torch.int32
+    return Layout(desc, m_cap, first, el,
+                  _empty((E,), i32, device), _empty((ep, E), i32, device),
+                  _empty((ep, ep), i32, device), _empty((ep, el), i32, device),
+                  _empty((ep,), i32, device), _empty((el + 1,), i32, device),
+                  _empty((T, k), i32, device), _empty((m_cap,), i32, device),
+                  _empty((max(layout_workspace_bytes(desc), 16),), torch.uint8, device))
+
+
+def layout(topk_idx: torch.Tensor, num_experts: int, ep_size: int = 1, local_rank: int = -1,
+           align: int = 128, out: Layout | None = None) -> Layout:
+    """Histogram, split plan, padded offsets and stable permutation (no host sync)."""
+    _need(topk_idx, "topk_idx", torch.int32)
+    T, k = topk_idx.shape
+    desc = layout_desc(T, num_experts, k, ep_size, local_rank, align)
+    L = alloc_layout(desc, topk_idx.device) if out is None else out
+    check("moe_layout", lib().moe_layout(
+        C.byref(desc), _ptr(topk_idx), _ptr(L.expert_counts), _ptr(L.send_counts),
+        _ptr(L.split_matrix), _ptr(L.recv_counts), _ptr(L.output_splits), _ptr(L.offsets),
+        _ptr(L.dst_row), _ptr(L.src_row), L.m_cap, _ptr(L.workspace), L.workspace.numel(),
+        _stream(topk_idx.device)))
+    return L
+
+
+def validate_layout(topk_idx: torch.Tensor, L: Layout) -> None:
+    """Debug check (synchronises): raises MoEError naming the first violation."""
+    buf = C.create_string_buffer(256)
+    st = lib().moe_validate_layout(C.byref(L.desc), _ptr(topk_idx), _ptr(L.offsets),
+                                   _ptr(L.dst_row), _ptr(L.src_row), L.m_cap,
+                                   _stream(topk_idx.device), buf, 256)
+    check("moe_validate_layout", st, buf.value.decode())
+
+
+# ---------------------------------------------------------------- permute
+
+def permute(x: torch.Tensor, dst_row: torch.Tensor, m_cap: int, out=None) -> torch.Tensor:
+    """x_perm [m_cap, H] bf16: row dst_row[t, s] holds x[t]; padding rows untouched."""
+    _need(x, "x", torch.bfloat16)
+    T, H = x.shape
+    _need(dst_row, "dst_row", torch.int32)
+    k = dst_row.shape[1]
+    out = _empty((m_cap, H), torch.bfloat16, x.device) if out is None else out
+    _need(out, "x_perm", torch.bfloat16, (m_cap, H))
+    check("moe_permute", lib().moe_permute(_ptr(x), T, H, k, _ptr(dst_row), m_cap, _ptr(out),
+                                           _stream(x.device)))
+    return out
+
+
+# ---------------------------------------------------------------- experts
+
+def pack_weights(w: torch.Tensor, out=None) -> torch.Tensor:
+    """[n, R, C] bf16 -> [n, C, R] (each matrix transposed), the GEMM's layout."""
+    _need(w, "w", torch.bfloat16)
+    n, R, Cc = w.shape
+    out = _empty((n, Cc, R), torch.bfloat16, w.device) if out is None else out
+    _need(out, "wt", torch.bfloat16, (n, Cc, R))
+    check("moe_pack_weights", lib().moe_pack_weights(_ptr(w), n, R, Cc, _ptr(out),
+                                                     _stream(w.device)))
+    return out
+
+
+def _gemm_common(a, offsets, counts):
+    _need(a, "activations", torch.bfloat16)
+    _need(offsets, "offsets", torch.int32)
+    if counts.dtype != torch.int32 or counts.device.type != "cuda" or not counts.is_contiguous():
+        raise TypeError("counts must be a contiguous int32 GPU tensor")
+    return offsets.numel() - 1
+
+
+def grouped_gate_up(x_perm, offsets, counts, w1t, w3t, out=None):
+    """h = silu(x W1) * (x W3) per local expert group; w1t/w3t are [E_loc, I, H]."""
+    e_loc = _gemm_common(x_perm, offsets, counts)
+    m_cap, H = x_perm.shape
+    I = w1t.shape[1]
+    _need(w1t, "w1t", torch.bfloat16, (e_loc, I, H))
+    _need(w3t, "w3t", torch.bfloat16, (e_loc, I, H))
+    out = _empty((m_cap, I), torch.bfloat16, x_perm.device) if out is None else out
+    _need(out, "h", torch.bfloat16, (m_cap, I))
+    check("moe_grouped_gate_up", lib().moe_grouped_gate_up(
+        _ptr(x_perm), _ptr(offsets), _ptr(counts), e_loc, m_cap, H, I, _ptr(w1t), _ptr(w3t),
+        _ptr(out), _stream(x_perm.device)))
+    return out
+
+
+def grouped_down(h, offsets, counts, w2t, out=None):
+    """y = h W2 per local expert group; w2t is [E_loc, H, I]."""
+    e_loc = _gemm_common(h, offsets, counts)
+    m_cap, I = h.shape
+    H = w2t.shape[1]
+    _need(w2t, "w2t", torch.bfloat16, (e_loc, H, I))
+    out = _empty((m_cap, H), torch.bfloat16, h.device) if out is None else out
+    _need(out, "y", torch.bfloat16, (m_cap, H))
+    check("moe_grouped_down", lib().moe_grouped_down(
+        _ptr(h), _ptr(offsets), _ptr(counts), e_loc, m_cap, I, H, _ptr(w2t), _ptr(out),
+        _stream(h.device)))
+    return out
+
+
+def grouped_swiglu(x_perm, offsets, counts, w1t, w3t, w2t, h=None, out=None):
+    """y = (silu(x W1) * (x W3)) W2 per local expert group, through workspace h."""
+    e_loc = _gemm_common(x_perm, offsets, counts)
+    m_cap, H = x_perm.shape
+    I = w1t.shape[1]
+    _need(w1t, "w1t", torch.bfloat16, (e_loc, I, H))
+    _need(w3t, "w3t", torch.bfloat16, (e_loc, I, H))
+    _need(w2t, "w2t", torch.bfloat16, (e_loc, H, I))
+    h = _empty((m_cap, I), torch.bfloat16, x_perm.device) if h is None else h
+    out = _empty((m_cap, H), torch.bfloat16, x_perm.device) if out is None else out
+    _need(h, "h", torch.bfloat16, (m_cap, I))
+    _need(out, "y", torch.bfloat16, (m_cap, H))
+    check("moe_grouped_swiglu", lib().moe_grouped_swiglu(
+        _ptr(x_perm), _ptr(offsets), _ptr(counts), e_loc, m_cap, H, I, _ptr(w1t), _ptr(w3t),
+        _ptr(w2t), _ptr(h), _ptr(out), _stream(x_perm.device)))
+    return out
+
+
+# ---------------------------------------------------------------- combine
+
+def combine(y: torch.Tensor, dst_row: torch.Tensor, topk_w: torch.Tensor, out=None):
+    """out [T, H] bf16 = sum_s topk_w[t, s] * y[dst_row[t, s]] (fp32 accumulate)."""
+    _need(y, "y", torch.bfloat16)
+    _need(dst_row, "dst_row", torch.int32)
+    T, k = dst_row.shape
+    _need(topk_w, "topk_w", torch.float32, (T, k))
+    H = y.shape[1]
+    out = _empty((T, H), torch.bfloat16, y.device) if out is None else out
+    _need(out, "out", torch.bfloat16, (T, H))
+    check("moe_combine", lib().moe_combine(_ptr(y), y.shape[0], _ptr(dst_row), _ptr(topk_w), T,
+                                           H, k, _ptr(out), _stream(y.device)))
+    return out

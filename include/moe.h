@@ -1,0 +1,253 @@
+/*
+ * moe.h -- C ABI of libmoe.so, the single-GPU MoE-layer hot path for AMD
+ * Instinct MI355X (gfx950):
+ *
+ *   moe_route -> moe_layout -> moe_permute -> moe_grouped_swiglu -> moe_combine
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Every pointer argument named *_d is DEVICE memory on the current HIP
+ *   device; descriptors (moe_layout_desc) are HOST memory. The caller owns
+ *   and allocates every buffer; the library allocates nothing, keeps no state
+ *   between calls and never blocks the host (moe_validate_layout excepted).
+ * - `stream` is a hipStream_t (NULL = the default stream). Each call only
+ *   enqueues kernels on it and returns; results are ready when the stream
+ *   reaches that point. Calls on different streams may run concurrently as
+ *   long as they do not share output buffers.
+ * - bf16 buffers hold IEEE bfloat16 bit patterns (uint16); float is fp32;
+ *   indices are int32. Matrices are row-major and densely packed.
+ * - Return value: a moe_status. Argument checks run on the host before any
+ *   launch: a call that returns anything but MOE_OK has enqueued nothing.
+ *   MOE_ERR_HIP reports a failed launch (hipGetLastError after the launch).
+ * - Data errors (an expert id out of [0, E), a row index past the end of a
+ *   buffer) are not diagnosed on the fast path; the kernels skip such
+ *   entries so every access stays in bounds. moe_validate_layout reports them.
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_ARG = 1,          /* null pointer, size out of range, misaligned buffer,
+                               workspace or m_cap too small */
+  MOE_ERR_UNSUPPORTED = 2,  /* a shape the kernels do not implement (see each call) */
+  MOE_ERR_HIP = 3,          /* a HIP runtime call or kernel launch failed */
+  MOE_ERR_COVERAGE = 4,     /* validator: a (token, slot) is missing or covered twice */
+  MOE_ERR_EXPERT_ID = 5,    /* validator: expert id out of range or repeated in a token */
+  MOE_ERR_LAYOUT = 6        /* validator: offsets / src_row / dst_row inconsistent */
+} moe_status;
+
+/* Static name of a status code ("MOE_OK", ...); never NULL. */
+const char* moe_status_string(int32_t status);
+
+/* ABI version of this header; bumped on any incompatible change. */
+int32_t moe_abi_version(void);
+
+/*
+ * moe_route -- token-choice top-k routing.
+ *
+ * Follows the token-choice top-k router of the AutoEP runtime (DeepSpeed
+ * AutoEP commit text, section "Attribution": ep_router.py after TorchTitan's
+ * TokenChoiceTopKRouter; section "Design", runtime step 2), with distinct
+ * experts per token (DeepSpeed PR #8847, section "Benchmark") and FP32
+ * routing weights kept in the router dtype (same page, section "Change").
+ * Per token t: the k experts with the largest logits[t, :], in descending
+ * order, ties to the lower expert id (-0.0 equals +0.0); weights are the
+ * softmax over all E experts renormalised over the k selected, computed as
+ * exp(l_j - l_max) / sum_selected exp(l_i - l_max) in fp32.
+ *
+ *   logits_d    [T, E] float, finite values
+ *   topk_idx_d  [T, k] int32 (out)
+ *   topk_w_d    [T, k] float (out)
+ * Limits: T >= 0, 1 <= E <= 1024, 1 <= k <= min(E, 16). T = 0 is a no-op.
+ */
+int32_t moe_route(const float* logits_d, int64_t num_tokens, int32_t num_experts,
+                  int32_t top_k, int32_t* topk_idx_d, float* topk_w_d, void* stream);
+
+/*
+ * Layout of one GPU's share when `ep_size` virtual ranks split the work:
+ * source rank s owns tokens [s*T/ep, (s+1)*T/ep); destination rank d owns
+ * experts [d*E/ep, (d+1)*E/ep); this GPU is destination `local_rank`
+ * (-1: every expert is local, E_loc = E; otherwise E_loc = E/ep).
+ */
+typedef struct moe_layout_desc {
+  int64_t num_tokens;  /* T, a multiple of ep_size */
+  int32_t num_experts; /* E, a multiple of ep_size, <= 1024 */
+  int32_t top_k;       /* k, 1..min(E, 16) */
+  int32_t ep_size;     /* >= 1, <= 64 */
+  int32_t local_rank;  /* -1 or 0..ep_size-1 */
+  int32_t align;       /* row alignment of each local expert's group, power of two <= 1024 */
+} moe_layout_desc;
+
+/* Worst-case local rows: T*min(k, E_loc) + E_loc*(align-1). Returns -1 for
+ * an invalid descriptor. Size src_row_d, x_perm, h and y with it. */
+int64_t moe_layout_m_cap(const moe_layout_desc* desc);
+
+/* Bytes of device workspace moe_layout needs (0 for an invalid descriptor). */
+size_t moe_layout_workspace_bytes(const moe_layout_desc* desc);
+
+/*
+ * moe_layout -- dispatch layout from topk_idx, with no host sync.
+ *
+ * The layout is computed from topk_idx and the expert count before any data
+ * moves (DeepEP issue #272, the maintainer's dispatch example:
+ * get_dispatch_layout, then dispatch), its histogram must not force a host
+ * sync (xtuner PR #2056, review comments: histc kept over bincount), and the
+ * split plan comes from the per-expert count matrix alone, its row sums being
+ * the splits (DeepSpeed PR #8190 "Derive AutoEP rank splits from the
+ * per-expert count exchange", sections "Redundancy" and "Fix"). Rows are
+ * grouped by local expert and each group is padded to `align` for the
+ * grouped GEMM (DeepSpeed AutoEP commit text, section "Attribution": token
+ * group alignment / padding helpers). Rows are named by the flat index
+ * token*top_k + slot (DeepSpeed PR #8847, section "Change").
+ *
+ * Outputs (all int32, device):
+ *   expert_counts_d [E]            assignments per expert (all E)
+ *   send_counts_d   [ep, E]        [s, e]: assignments of source s to expert e
+ *   split_matrix_d  [ep, ep]       [s, d]: assignments of source s to destination d
+ *                                  (row sums: input splits; column local_rank: output splits)
+ *   recv_counts_d   [ep, E_loc]    [s, e]: assignments of source s to local expert e
+ *   output_splits_d [ep]           recv_counts row sums
+ *   offsets_d       [E_loc + 1]    offsets[0] = 0, offsets[e+1] = offsets[e] + ceil(c_e/align)*align
+ *   dst_row_d       [T, k]         local row of (t, slot), or -1 if its expert is not local
+ *   src_row_d       [m_cap]        flat index t*k+slot held by a row; -1 for padding and
+ *                                  for every row from offsets[E_loc] to m_cap
+ * Within an expert's group, rows follow ascending flat index (a stable
+ * order, independent of thread scheduling).
+ *   topk_idx_d      [T, k] int32 expert ids; ids outside [0, E) are skipped.
+ *   m_cap           >= moe_layout_m_cap(desc)
+ *   workspace_d     >= moe_layout_workspace_bytes(desc) bytes, 16-byte aligned;
+ *                   contents on entry do not matter.
+ * Any output pointer except offsets_d, dst_row_d and src_row_d may be NULL
+ * to skip it.
+ */
+int32_t moe_layout(const moe_layout_desc* desc, const int32_t* topk_idx_d,
+                   int32_t* expert_counts_d, int32_t* send_counts_d,
+                   int32_t* split_matrix_d, int32_t* recv_counts_d,
+                   int32_t* output_splits_d, int32_t* offsets_d, int32_t* dst_row_d,
+                   int32_t* src_row_d, int64_t m_cap, void* workspace_d,
+                   size_t workspace_bytes, void* stream);
+
+/*
+ * moe_permute -- expert-major token gather (the local part of dispatch).
+ *
+ * The reorder-by-expert step of the AutoEP flow (DeepSpeed AutoEP commit
+ * text, section "Design", runtime step 3) and the local half of DeepEP's
+ * dispatch (DeepEP issue #272: x, topk_idx, topk_weights in; rows grouped per
+ * expert out). For every (t, slot) with dst_row[t, slot] = r >= 0:
+ * x_perm[r, :] = x[t, :], a bit copy. Padding rows are not written; the
+ * grouped GEMM does not read them.
+ *   x_d       [T, H] bf16, 16-byte aligned
+ *   dst_row_d [T, k] int32 (from moe_layout); rows >= m_cap are skipped
+ *   x_perm_d  [m_cap, H] bf16 (out), 16-byte aligned
+ * Limits: H a multiple of 8, 8 <= H <= 16384; 1 <= k <= 16.
+ */
+int32_t moe_permute(const void* x_d, int64_t num_tokens, int32_t hidden, int32_t top_k,
+                    const int32_t* dst_row_d, int64_t m_cap, void* x_perm_d,
+                    void* stream);
+
+/*
+ * moe_pack_weights -- one-time repack of expert matrices to the layout the
+ * grouped GEMM reads: wt[e, c, r] = w[e, r, c] for e < num_mats, a bit copy.
+ * Expert weights arrive in math orientation (gate/up [E, H, I], down
+ * [E, I, H]); the GEMM wants each expert's matrix output-major with the
+ * reduction dimension contiguous (gate/up [E, I, H], down [E, H, I]). This is
+ * the load-time conversion into the grouped expert layout the runtime
+ * expects (DeepSpeed AutoEP commit text, section "Design": ep_repack.py),
+ * done once per weight set, outside the per-step path.
+ *   w_d  [num_mats, rows, cols] bf16;  wt_d [num_mats, cols, rows] bf16 (out)
+ */
+int32_t moe_pack_weights(const void* w_d, int64_t num_mats, int32_t rows, int32_t cols,
+                         void* wt_d, void* stream);
+
+/*
+ * Grouped SwiGLU expert MLPs over ragged expert groups (local grouped expert
+ * compute of the AutoEP flow, DeepSpeed AutoEP commit text, sections
+ * "Attribution" (ep_experts.py, grouped-GEMM execution) and "Design",
+ * runtime step 5; bf16 grouped GEMM as in DeepSpeed PR #8847, section
+ * "Tests"). For local expert e the rows [offsets[e], offsets[e] + counts[e])
+ * of the input go through expert e:
+ *
+ *   moe_grouped_gate_up:  h = silu(x_perm W1[e]) * (x_perm W3[e])   (fp32 math, bf16 out)
+ *   moe_grouped_down:     y = h W2[e]                               (fp32 accumulate, bf16 out)
+ *   moe_grouped_swiglu:   both, in that order, through the caller's h buffer
+ *
+ * silu(a) = a / (1 + e^-a). Products are bf16 x bf16 on the matrix cores,
+ * accumulated in fp32, rounded to bf16 (nearest even) once at the end.
+ * Rows outside every [offsets[e], offsets[e] + counts[e]) are neither read
+ * nor written.
+ *   x_perm_d   [m_cap, H] bf16          h_d [m_cap, I] bf16        y_d [m_cap, H] bf16
+ *   offsets_d  [E_loc + 1] int32        counts_d [E_loc] int32 (local expert counts,
+ *                                       = expert_counts_d + first local expert)
+ *   w1t_d, w3t_d [E_loc, I, H] bf16     w2t_d [E_loc, H, I] bf16  (moe_pack_weights layout)
+ * Limits: H and I multiples of 128; E_loc <= 1024; offsets[E_loc] <= m_cap.
+ * All bf16 pointers 16-byte aligned. Unsupported shapes: MOE_ERR_UNSUPPORTED.
+ */
+int32_t moe_grouped_gate_up(const void* x_perm_d, const int32_t* offsets_d,
+                            const int32_t* counts_d, int32_t num_local_experts,
+                            int64_t m_cap, int32_t hidden, int32_t inter,
+                            const void* w1t_d, const void* w3t_d, void* h_d, void* stream);
+
+int32_t moe_grouped_down(const void* h_d, const int32_t* offsets_d, const int32_t* counts_d,
+                         int32_t num_local_experts, int64_t m_cap, int32_t inter,
+                         int32_t hidden, const void* w2t_d, void* y_d, void* stream);
+
+int32_t moe_grouped_swiglu(const void* x_perm_d, const int32_t* offsets_d,
+                           const int32_t* counts_d, int32_t num_local_experts,
+                           int64_t m_cap, int32_t hidden, int32_t inter,
+                           const void* w1t_d, const void* w3t_d, const void* w2t_d,
+                           void* h_d, void* y_d, void* stream);
+
+/*
+ * moe_combine -- fused weighted-sum restore.
+ *
+ * The fused restore of DeepSpeed PR #8847 ("AutoEP: support
+ * combine_impl=fused_weighted_sum ...", sections "Problem" and "Change"):
+ * each row is addressed by the flat index token*top_k + slot, the routing
+ * weights stay FP32 in a [tokens, top_k] layout, and weight x row products
+ * are accumulated in FP32 (section "Benchmark": the error left is the bf16
+ * output rounding). Per token t:
+ *
+ *   out[t, :] = bf16( sum over slots s = 0..k-1 with 0 <= dst_row[t, s] < y_rows
+ *                     of topk_w[t, s] * y[dst_row[t, s], :] )
+ *
+ * summed in fp32 in slot order (fused multiply-add), rounded once to bf16
+ * (nearest even). A token with no local slot gets a zero row. The result
+ * does not depend on where the rows sit in y.
+ *   y_d       [y_rows, H] bf16, 16-byte aligned
+ *   dst_row_d [T, k] int32;  topk_w_d [T, k] float
+ *   out_d     [T, H] bf16 (out), 16-byte aligned
+ * Limits: H a multiple of 8, 8 <= H <= 16384; 1 <= k <= 16.
+ */
+int32_t moe_combine(const void* y_d, int64_t y_rows, const int32_t* dst_row_d,
+                    const float* topk_w_d, int64_t num_tokens, int32_t hidden,
+                    int32_t top_k, void* out_d, void* stream);
+
+/*
+ * moe_validate_layout -- debug check of a layout (SYNCHRONISES the stream,
+ * copies the buffers to the host and checks there). Mirrors the fused
+ * restore's coverage check (DeepSpeed PR #8847, section "Change": a missing
+ * (token, slot) raises instead of reading an unset row).
+ * Returns MOE_OK, MOE_ERR_EXPERT_ID (id out of range or repeated in a token),
+ * MOE_ERR_COVERAGE (a local (t, slot) without a row, or a row claimed twice) or
+ * MOE_ERR_LAYOUT (offsets not aligned/monotone, src_row and dst_row not
+ * inverse, padding or order wrong). `detail` (may be NULL) receives a
+ * NUL-terminated message of at most detail_len bytes.
+ */
+int32_t moe_validate_layout(const moe_layout_desc* desc, const int32_t* topk_idx_d,
+                            const int32_t* offsets_d, const int32_t* dst_row_d,
+                            const int32_t* src_row_d, int64_t m_cap, void* stream,
+                            char* detail, size_t detail_len);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H_ */

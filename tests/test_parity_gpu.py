@@ -1,0 +1,408 @@
+"""GPU parity: every stage of the HIP path, called through the C ABI (via the
+ctypes binding), against the CPU oracle on the same seeded inputs.
+
+Bars: bit-exact for topk_idx, counts, splits, offsets, dst_row, src_row and
+permuted rows; routing weights within 1e-6; the combine within 1 bf16 ulp of
+the fp64 oracle given the same expert outputs; expert outputs and the whole
+layer within max|gpu - oracle| / max|oracle| <= 1e-2.
+
+Small workloads are compared element by element in full; the large ones
+(the Mixtral-, Qwen3-MoE- and DeepSeek-V3-shaped layers, in the same launch
+configuration the benchmark times) on rows and tokens sampled with a fixed
+seed, plus the integer outputs in full.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from workloads import MoEConfig
+from oracle import bf16 as obf16, checks, combine as ocombine, experts as oexperts
+from oracle import layer as olayer, layout as olayout, permute as opermute, route as oroute
+
+from gpu_util import Case, bits, f64, from_bits, i32, rel_max, ulp_distance
+
+pytestmark = pytest.mark.gpu
+
+moe = pytest.importorskip("combine_top_router_amd")
+
+# extra shapes: ragged tails, several layout tiles per rank, edge cases
+EXTRA = {
+    "ragged": MoEConfig(name="ragged", num_tokens=3000, hidden=384, num_experts=16, top_k=4,
+                        inter=256, ep_size=4, local_rank=2, align=128,
+                        dists=("mild",), shares=(-1, 2)),
+    "top1_odd": MoEConfig(name="top1_odd", num_tokens=37, hidden=128, num_experts=4, top_k=1,
+                          inter=128, ep_size=1, local_rank=-1, align=16),
+    "wide": MoEConfig(name="wide", num_tokens=256, hidden=128, num_experts=1024, top_k=16,
+                      inter=128, ep_size=1, local_rank=-1, align=128, dists=("zipf",)),
+}
+
+
+def cfg_of(name):
+    return EXTRA[name] if name in EXTRA else workloads.get(name)
+
+
+FULL = {"tiny", "ragged", "top1_odd", "wide"}  # oracle runs these whole
+
+CASES = [("tiny", "balanced", s) for s in (-1, 0, 1)]
+CASES += [("ragged", "mild", -1), ("ragged", "mild", 2), ("top1_odd", "balanced", -1),
+          ("wide", "zipf", -1)]
+CASES += [("mixtral_8x7b", "balanced", -1), ("qwen3_30b_a3b", "zipf", -1)]
+CASES += [("deepseek_v3_ep8_share", d, 0) for d in ("balanced", "mild", "severe")]
+CASES += [("deepseek_v3_large", "severe", -1)]
+IDS = [f"{c}-{d}-r{s}" for c, d, s in CASES]
+
+
+def announce(*what):
+    print("CASE", *what, flush=True)
+
+
+_case_cache = {}
+
+
+def get_case(name, dist, share, weights=True):
+    key = (name, dist, share, weights)
+    if key not in _case_cache:
+        _case_cache.clear()
+        torch.cuda.empty_cache()
+        _case_cache[key] = Case(cfg_of(name), dist, share, weights=weights)
+    return _case_cache[key]
+
+
+_oracle_cache = {}
+
+
+def oracle_routing(case):
+    key = (case.cfg.name, case.dist, case.local_rank)
+    if key not in _oracle_cache:
+        _oracle_cache.clear()
+        cfg = case.cfg
+        idx, w = oroute.route(case.logits_np(), cfg.top_k)
+        L = olayout.layout(idx, cfg.num_experts, cfg.ep_size, case.local_rank, cfg.align,
+                           cfg.m_cap(case.local_rank))
+        _oracle_cache[key] = (idx, w, L)
+    return _oracle_cache[key]
+
+
+# ---------------------------------------------------------------- route
+
+@pytest.mark.parametrize("name,dist,share", CASES, ids=IDS)
+def test_route(name, dist, share):
+    announce("route", name, dist, share)
+    case = get_case(name, dist, share, weights=False)
+    idx, w = moe.route(case.logits, case.cfg.top_k)
+    want_idx, want_w = oracle_routing(case)[:2]
+    got_idx = idx.cpu().numpy()
+    assert (got_idx == want_idx).all(), np.argwhere(got_idx != want_idx)[:5]
+    assert np.abs(w.cpu().numpy() - want_w).max() <= 1e-6
+
+
+def test_route_ties_and_signed_zero():
+    announce("route ties")
+    logits = np.array([[3, 1, 2, 0], [0, 0, 5, 5], [1, 4, 0, 4], [2, 0, 2, 0],
+                       [-0.0, 0.0, -1, -1], [0.0, -0.0, -1, -1]], np.float32)
+    idx, w = moe.route(torch.from_numpy(logits).cuda(), 2)
+    want_idx, want_w = oroute.route(logits, 2)
+    assert (idx.cpu().numpy() == want_idx).all()
+    assert np.abs(w.cpu().numpy() - want_w).max() <= 1e-6
+
+
+def test_route_equal_logits_and_k_equals_e():
+    announce("route equal logits")
+    logits = torch.full((5, 16), 0.5, device="cuda")
+    idx, w = moe.route(logits, 16)
+    assert (idx.cpu().numpy() == np.arange(16)).all()
+    assert np.abs(w.cpu().numpy() - 1 / 16).max() <= 1e-7
+
+
+# ---------------------------------------------------------------- layout
+
+LAYOUT_KEYS = ("expert_counts", "send_counts", "split_matrix", "recv_counts", "output_splits",
+               "offsets", "dst_row", "src_row")
+
+
+@pytest.mark.parametrize("name,dist,share", CASES, ids=IDS)
+def test_layout(name, dist, share):
+    announce("layout", name, dist, share)
+    case = get_case(name, dist, share, weights=False)
+    cfg = case.cfg
+    idx, _, want = oracle_routing(case)
+    idx_d = i32(idx)
+    L = moe.layout(idx_d, cfg.num_experts, cfg.ep_size, share, cfg.align)
+    assert L.m_cap == want["m_cap"]
+    for k in LAYOUT_KEYS:
+        got = getattr(L, k).cpu().numpy()
+        assert (got == want[k]).all(), (k, np.argwhere(got != want[k])[:5])
+    moe.validate_layout(idx_d, L)
+
+
+def test_layout_every_share_covers_each_slot_once():
+    announce("layout coverage over shares")
+    cfg = workloads.get("deepseek_v3_ep8_share")
+    case = get_case(cfg.name, "severe", 0, weights=False)
+    idx = moe.route(case.logits, cfg.top_k)[0]
+    dsts = []
+    for d in range(cfg.ep_size):
+        L = moe.layout(idx, cfg.num_experts, cfg.ep_size, d, cfg.align)
+        moe.validate_layout(idx, L)
+        dsts.append(L.dst_row.cpu().numpy())
+        assert (L.split_matrix[:, d] == L.output_splits).all()
+    checks.check_coverage(dsts, cfg.num_tokens, cfg.top_k)
+
+
+def test_layout_zero_tokens():
+    announce("layout T=0")
+    idx = torch.empty((0, 2), dtype=torch.int32, device="cuda")
+    L = moe.layout(idx, 8, 1, -1, 128)
+    assert (L.offsets.cpu() == 0).all() and (L.expert_counts.cpu() == 0).all()
+    assert (L.src_row.cpu() == -1).all()
+
+
+def test_layout_all_to_one_expert():
+    announce("layout one hot expert")
+    T, k, E = 5000, 1, 64
+    idx = np.full((T, k), 7, np.int32)
+    want = olayout.layout(idx, E, 1, -1, 128)
+    L = moe.layout(i32(idx), E, 1, -1, 128)
+    for key in LAYOUT_KEYS:
+        assert (getattr(L, key).cpu().numpy() == want[key]).all(), key
+
+
+def test_validator_reports_bad_input():
+    announce("validator")
+    idx = np.array([[0, 1], [1, 2], [2, 3], [3, 0]], np.int32)
+    L = moe.layout(i32(idx), 4, 1, -1, 4)
+    moe.validate_layout(i32(idx), L)
+    bad = idx.copy()
+    bad[2, 1] = 9  # out of range: the layout skips it, the validator names it
+    with pytest.raises(moe.MoEError, match="EXPERT_ID"):
+        moe.validate_layout(i32(bad), moe.layout(i32(bad), 4, 1, -1, 4))
+    dup = idx.copy()
+    dup[1, 1] = 1  # a token repeating an expert
+    with pytest.raises(moe.MoEError, match="EXPERT_ID"):
+        moe.validate_layout(i32(dup), moe.layout(i32(dup), 4, 1, -1, 4))
+    L.dst_row[3, 0] = -1  # drop one (token, slot): uncovered
+    with pytest.raises(moe.MoEError, match="COVERAGE"):
+        moe.validate_layout(i32(idx), L)
+
+
+# ---------------------------------------------------------------- permute
+
+def _sample_rows(L, rng, n=2048):
+    rows = np.nonzero(L["src_row"] >= 0)[0]
+    if rows.size > n:
+        rows = np.sort(np.concatenate([rng.choice(rows, n - 2, replace=False),
+                                       rows[[0, -1]]]))
+    return rows
+
+
+@pytest.mark.parametrize("name,dist,share", CASES, ids=IDS)
+def test_permute(name, dist, share):
+    announce("permute", name, dist, share)
+    case = get_case(name, dist, share, weights=False)
+    cfg = case.cfg
+    idx, _, L = oracle_routing(case)
+    sentinel = 0x7FC1  # a NaN pattern: padding rows must keep it
+    xp = torch.full((L["m_cap"], cfg.hidden), 0, dtype=torch.int16, device="cuda")
+    xp.fill_(sentinel)
+    xp = xp.view(torch.bfloat16)
+    moe.permute(case.x, i32(L["dst_row"]), L["m_cap"], out=xp)
+    rng = np.random.default_rng(0)
+    rows = _sample_rows(L, rng) if name not in FULL else np.nonzero(L["src_row"] >= 0)[0]
+    want = opermute.permute(bits(case.x), L["src_row"], cfg.top_k, rows)
+    got = bits(xp[torch.as_tensor(rows, device="cuda")])
+    assert (got == want).all()
+    pad = np.nonzero(L["src_row"][:L["offsets"][-1]] < 0)[0][:512]
+    if pad.size:
+        assert (bits(xp[torch.as_tensor(pad, device="cuda")]) == sentinel).all()
+
+
+# ---------------------------------------------------------------- grouped SwiGLU
+
+def _gemm_rows(L, rng, full):
+    counts = L["local_counts"]
+    if full:
+        return np.nonzero(L["src_row"] >= 0)[0]
+    nz = np.nonzero(counts)[0]
+    pick = {int(nz[np.argmax(counts[nz])]), int(nz[np.argmin(counts[nz])]),
+            int(nz[len(nz) // 2])}
+    rows = []
+    for e in sorted(pick):
+        a, c = int(L["offsets"][e]), int(counts[e])
+        r = list(rng.choice(c, min(c, 6), replace=False)) + [c - 1, min(c - 1, 127), 0]
+        rows += [a + int(v) for v in set(r)]
+    return np.array(sorted(set(rows)))
+
+
+@pytest.mark.parametrize("name,dist,share", CASES, ids=IDS)
+def test_grouped_swiglu(name, dist, share):
+    announce("grouped_swiglu", name, dist, share)
+    case = get_case(name, dist, share)
+    cfg = case.cfg
+    idx, _, L = oracle_routing(case)
+    m_cap, H, I = L["m_cap"], cfg.hidden, cfg.inter
+    src = torch.as_tensor(L["src_row"].astype(np.int64), device="cuda")
+    valid = src >= 0
+    # x_perm: the token rows at their oracle places, NaN everywhere else
+    xp = torch.full((m_cap, H), float("nan"), dtype=torch.bfloat16, device="cuda")
+    xp[valid] = case.x[src[valid] // cfg.top_k]
+    y = torch.full((m_cap, H), 0, dtype=torch.int16, device="cuda").fill_(0x7FC1)
+    y = y.view(torch.bfloat16)
+    h = torch.empty((m_cap, I), dtype=torch.bfloat16, device="cuda")
+    w1t, w3t, w2t = (moe.pack_weights(w) for w in (case.w1, case.w3, case.w2))
+    counts = i32(L["local_counts"])
+    moe.grouped_swiglu(xp, i32(L["offsets"]), counts, w1t, w3t, w2t, h=h, out=y)
+
+    rng = np.random.default_rng(1)
+    rows = _gemm_rows(L, rng, name in FULL)
+    xrows = f64(xp[torch.as_tensor(rows, device="cuda")])
+    seg = np.searchsorted(L["offsets"], rows, side="right") - 1
+    want = np.zeros((rows.size, H))
+    for e in np.unique(seg):
+        m = seg == e
+        want[m] = oexperts.swiglu(xrows[m], *case.weights_of(int(e)))
+    got = f64(y[torch.as_tensor(rows, device="cuda")])
+    assert np.isfinite(got).all()
+    assert rel_max(got, want) <= 1e-2, rel_max(got, want)
+    # padding rows of y are never written
+    pad = np.nonzero(L["src_row"][:L["offsets"][-1]] < 0)[0][:512]
+    if pad.size:
+        assert (bits(y[torch.as_tensor(pad, device="cuda")]) == 0x7FC1).all()
+
+
+def test_pack_weights_is_a_transpose():
+    announce("pack")
+    w = torch.randn((3, 384, 256), device="cuda").to(torch.bfloat16)
+    wt = moe.pack_weights(w)
+    assert (bits(wt) == bits(w).transpose(0, 2, 1)).all()
+
+
+def test_swiglu_orientation_closed_form():
+    # W1 = permutation, W3 = W2 = identity: y[:, j] = silu(x[:, pi(j)]) * x[:, j]
+    announce("swiglu orientation")
+    n, rows = 128, 200
+    rng = np.random.default_rng(3)
+    pi = rng.permutation(n)
+    P = np.zeros((n, n))
+    P[pi, np.arange(n)] = 1.0
+    eye = np.eye(n)
+    to_d = lambda a: from_bits(obf16.encode(a))[None]  # noqa: E731
+    x = obf16.round_to_bf16(rng.standard_normal((rows, n)))
+    offsets, counts = i32([0, 256]), i32([rows])
+    y = moe.grouped_swiglu(from_bits(obf16.encode(np.vstack([x, np.zeros((56, n))]))), offsets,
+                           counts, moe.pack_weights(to_d(P)), moe.pack_weights(to_d(eye)),
+                           moe.pack_weights(to_d(eye)))
+    want = oexperts.swiglu(x, P, eye, eye)
+    assert rel_max(f64(y[:rows]), want) <= 1e-2
+
+
+# ---------------------------------------------------------------- combine
+
+def _combine_tokens(cfg, rng, full):
+    return np.arange(cfg.num_tokens) if full else np.sort(
+        rng.choice(cfg.num_tokens, min(cfg.num_tokens, 1024), replace=False))
+
+
+@pytest.mark.parametrize("name,dist,share", CASES, ids=IDS)
+def test_combine(name, dist, share):
+    announce("combine", name, dist, share)
+    case = get_case(name, dist, share, weights=False)
+    cfg = case.cfg
+    idx, w, L = oracle_routing(case)
+    y = workloads.gen.expert_outputs(cfg, L["m_cap"], seed=5, device="cuda")
+    w32 = w.astype(np.float32)
+    out = moe.combine(y, i32(L["dst_row"]), torch.from_numpy(w32).cuda())
+    rng = np.random.default_rng(2)
+    toks = _combine_tokens(cfg, rng, name in FULL)
+    dst = L["dst_row"][toks]
+    rows = np.unique(dst[dst >= 0])
+    ysub = f64(y[torch.as_tensor(rows, device="cuda")])
+    remap = np.full(L["m_cap"], -1)
+    remap[rows] = np.arange(rows.size)
+    want = obf16.encode(ocombine.combine(ysub, np.where(dst >= 0, remap[dst], -1), w32[toks]))
+    got = bits(out[torch.as_tensor(toks, device="cuda")])
+    d = ulp_distance(got, want)
+    assert d.max() <= 1, (d.max(), np.argwhere(d > 1)[:5])
+    # tokens without a local slot come back as zero rows
+    none_local = (dst < 0).all(axis=1)
+    assert (got[none_local] & 0x7FFF == 0).all()
+
+
+def test_combine_invariant_under_row_shuffle():
+    announce("combine shuffle")
+    cfg = workloads.get("qwen3_30b_a3b")
+    case = get_case(cfg.name, "zipf", -1, weights=False)
+    idx, w, L = oracle_routing(case)
+    y = workloads.gen.expert_outputs(cfg, L["m_cap"], seed=6, device="cuda")
+    wt = torch.from_numpy(w.astype(np.float32)).cuda()
+    a = moe.combine(y, i32(L["dst_row"]), wt)
+    perm = torch.randperm(L["m_cap"], generator=torch.Generator().manual_seed(0)).cuda()
+    inv = torch.empty_like(perm)
+    inv[perm] = torch.arange(perm.numel(), device="cuda")
+    dst = torch.as_tensor(L["dst_row"].astype(np.int64), device="cuda")
+    dst2 = torch.where(dst >= 0, inv[dst.clamp(min=0)], dst).to(torch.int32)
+    b = moe.combine(y[perm].contiguous(), dst2, wt)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_combine_only_large():
+    # the combine on its own at the large DeepSeek-V3 shape: expert outputs
+    # [T*8, H] in expert order with no padding (alignment 1), severe skew
+    announce("combine-only large")
+    cfg = workloads.get("deepseek_v3_large")
+    case = get_case(cfg.name, "severe", -1, weights=False)
+    idx, w = oroute.route(case.logits_np(), cfg.top_k)
+    L = olayout.layout(idx, cfg.num_experts, 1, -1, 1)
+    n = cfg.num_tokens * cfg.top_k
+    y = workloads.gen.expert_outputs(cfg, n, seed=7, device="cuda")
+    w32 = w.astype(np.float32)
+    out = moe.combine(y, i32(L["dst_row"]), torch.from_numpy(w32).cuda())
+    rng = np.random.default_rng(4)
+    toks = np.sort(rng.choice(cfg.num_tokens, 512, replace=False))
+    dst = L["dst_row"][toks]
+    rows = np.unique(dst)
+    remap = np.full(n, -1)
+    remap[rows] = np.arange(rows.size)
+    want = obf16.encode(ocombine.combine(f64(y[torch.as_tensor(rows, device="cuda")]),
+                                         remap[dst], w32[toks]))
+    assert ulp_distance(bits(out[torch.as_tensor(toks, device="cuda")]), want).max() <= 1
+
+
+# ---------------------------------------------------------------- whole layer
+
+def _layer_tokens(case, idx, rng, full):
+    cfg = case.cfg
+    if full:
+        return np.arange(cfg.num_tokens)
+    local = ((idx >= case.first) & (idx < case.first + case.num_local)).any(axis=1)
+    cand = np.nonzero(local)[0]
+    n = 4 if cfg.name == "deepseek_v3_large" else 16
+    return np.sort(rng.choice(cand, min(n, cand.size), replace=False))
+
+
+@pytest.mark.parametrize("name,dist,share", CASES, ids=IDS)
+def test_layer(name, dist, share):
+    announce("layer", name, dist, share)
+    case = get_case(name, dist, share)
+    cfg = case.cfg
+    layer = moe.MoELayer(cfg.num_tokens, cfg.hidden, cfg.num_experts, cfg.top_k, cfg.inter,
+                         case.w1, case.w3, case.w2, cfg.ep_size, share, cfg.align)
+    out = layer(case.x, case.logits).clone()
+    idx, w, L = oracle_routing(case)
+    # integer outputs of the GPU pipeline: bit-exact
+    assert (layer.topk_idx.cpu().numpy() == idx).all()
+    for k in LAYOUT_KEYS:
+        assert (getattr(layer.L, k).cpu().numpy() == L[k]).all(), k
+    rng = np.random.default_rng(3)
+    toks = _layer_tokens(case, idx, rng, name in FULL)
+    want = olayer.token_outputs(toks, case.x_np(), idx, w, case.weights_of, case.first,
+                                case.num_local)
+    got = f64(out[torch.as_tensor(toks, device="cuda")])
+    assert np.isfinite(got).all()
+    assert rel_max(got, want) <= 1e-2, rel_max(got, want)
+    # running the layer again gives the same bits (no dependence on scheduling)
+    again = layer(case.x, case.logits)
+    assert torch.equal(out.view(torch.int16), again.view(torch.int16))
+    del layer

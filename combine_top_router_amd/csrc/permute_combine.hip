@@ -11,7 +11,7 @@
 //
 // combine: the fused weighted restore of DeepSpeed PR #8847 (sections
 //   "Problem", "Change", "Benchmark"): per token, sum over slots in slot order
-//   of fp32 weight x bf16 row in fp32 (fused multiply-add), one rounding to
+//   of fp32 weight x bf16 row, products and sums in fp32, one rounding to
 //   bf16; rows addressed through dst_row (flat index token*top_k + slot).
 #include "moe_internal.h"
 
@@ -75,6 +75,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const u32x4* __restrict__ 
                                                       const float* __restrict__ topk_w,
                                                       int64_t T, int hv, int k_rt,
                                                       u32x4* __restrict__ out) {
+  // fp32 product, then fp32 sum: two IEEE roundings per slot, never contracted
+  // to an FMA, so the result is the plain fp32 slot-order sum
+#pragma clang fp contract(off)
   const int k = K > 0 ? K : k_rt;
   constexpr int KM = K > 0 ? K : 16;
   const int64_t t = uniform(static_cast<int64_t>(blockIdx.x) * kTokensPerBlock +
@@ -111,7 +114,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const u32x4* __restrict__ 
       float f[8];
       unpack8(in[j], f);
 #pragma unroll
-      for (int q = 0; q < 8; ++q) acc[q] = __builtin_fmaf(w[j], f[q], acc[q]);
+      for (int q = 0; q < 8; ++q) acc[q] = acc[q] + w[j] * f[q];
     }
     __builtin_nontemporal_store(pack8(acc), dst + v);
   }

@@ -14,11 +14,16 @@ combine_impl=fused_weighted_sum with AutoEP+AutoTP folding"):
 * section "Benchmark": the fused output's error against an FP64 reference is
   the rounding of the bf16 output itself.
 
-So the oracle sums in fp64, in slot order, and rounds once to bf16. A slot
-whose row lives on another GPU share has ``dst_row = -1`` and contributes
-nothing; a token with no local slot gives a zero row. ``restore_default``
-is the activation-dtype restore of section "Problem", kept for the error
-contrast of section "Benchmark".
+The pages fix the precision of this step, so ``combine`` is the FP32 sum:
+each product ``w * y`` is an fp32 multiplication, each partial sum an fp32
+addition, slots added in order 0..k-1 starting from zero, and the result is
+rounded once to bf16 (reading: "accumulates in FP32" taken literally, IEEE
+fp32 operations, no fused multiply-add). A slot whose row lives on another
+GPU share has ``dst_row = -1`` and contributes nothing; a token with no local
+slot gives a zero row. ``combine_exact`` is the same sum in fp64, the
+reference the pages measure the error against; ``restore_default`` is the
+activation-dtype restore of section "Problem", kept for the error contrast
+of section "Benchmark".
 """
 from __future__ import annotations
 
@@ -27,28 +32,50 @@ import numpy as np
 from . import bf16
 
 
-def combine(y, dst_row, topk_w, validate_coverage: bool = False) -> np.ndarray:
-    """out [T, H] float64 (unrounded): sum over slots s with dst_row[t, s] >= 0
-    of topk_w[t, s] * y[dst_row[t, s]], added in slot order."""
-    y = np.asarray(y, dtype=np.float64)
-    dst = np.asarray(dst_row, dtype=np.int64)
-    w = np.asarray(topk_w, dtype=np.float64)
-    T, k = dst.shape
+def _coverage(dst, validate_coverage):
     if validate_coverage and (dst < 0).any():
         t, s = np.argwhere(dst < 0)[0]
         raise RuntimeError(f"(token {t}, slot {s}) is not covered by any expert row")
+
+
+def combine(y, dst_row, topk_w, validate_coverage: bool = False) -> np.ndarray:
+    """out [T, H] float32 (before the bf16 rounding): slots s with
+    dst_row[t, s] >= 0 contribute topk_w[t, s] * y[dst_row[t, s]], the weight
+    taken as fp32, product and running sum each rounded to fp32, slot order."""
+    y32 = np.asarray(y).astype(np.float32)
+    dst = np.asarray(dst_row, dtype=np.int64)
+    w32 = np.asarray(topk_w).astype(np.float32)
+    _coverage(dst, validate_coverage)
+    T, k = dst.shape
+    out = np.zeros((T, y32.shape[1]), dtype=np.float32)
+    for s in range(k):
+        r = dst[:, s]
+        m = r >= 0
+        prod = w32[m, s][:, None] * y32[r[m]]  # fp32 products
+        out[m] = out[m] + prod  # fp32 sums
+    return out
+
+
+def combine_bf16(y, dst_row, topk_w, validate_coverage: bool = False) -> np.ndarray:
+    """The fused restore's output: the FP32 sum rounded once to bf16 (nearest
+    even), returned as float64 values."""
+    return bf16.round_to_bf16(combine(y, dst_row, topk_w, validate_coverage).astype(np.float64))
+
+
+def combine_exact(y, dst_row, topk_w, validate_coverage: bool = False) -> np.ndarray:
+    """The same weighted sum in fp64 (unrounded), the reference of the error
+    figures."""
+    y = np.asarray(y, dtype=np.float64)
+    dst = np.asarray(dst_row, dtype=np.int64)
+    w = np.asarray(topk_w, dtype=np.float64)
+    _coverage(dst, validate_coverage)
+    T, k = dst.shape
     out = np.zeros((T, y.shape[1]), dtype=np.float64)
     for s in range(k):
         r = dst[:, s]
         m = r >= 0
         out[m] += w[m, s][:, None] * y[r[m]]
     return out
-
-
-def combine_bf16(y, dst_row, topk_w, validate_coverage: bool = False) -> np.ndarray:
-    """The fused restore's output: fp64 sum, one round-to-nearest-even to bf16
-    (returned as float64 values)."""
-    return bf16.round_to_bf16(combine(y, dst_row, topk_w, validate_coverage))
 
 
 def restore_default(y, dst_row, topk_w) -> np.ndarray:

@@ -4,7 +4,10 @@ commit text, section "Design": route, reorder by expert, dispatch, local
 grouped expert compute, combine and restore the original order), with the
 cross-GPU all-to-all steps absent because one GPU runs its own share.
 
-``token_outputs`` gives the same result for a few tokens at a time, straight
+The layer's output is the exact (fp64) weighted sum of fp64 expert outputs;
+the bf16 rounding of expert outputs on the GPU and its FP32 combine are
+covered by the layer tolerance. ``token_outputs`` gives the same result for a
+few tokens at a time, straight
 from the definition (the sum over a token's local slots of weight times its
 expert's SwiGLU output), for sampling layers too large to run whole.
 """
@@ -23,7 +26,7 @@ def layer(x, logits, top_k: int, weights_of, num_experts: int, ep_size: int = 1,
     L = layout.layout(idx, num_experts, ep_size, local_rank, align, m_cap)
     xp = permute.permute(np.asarray(x, dtype=np.float64), L["src_row"], top_k)
     y = experts.grouped_swiglu(xp, L["offsets"], L["local_counts"], weights_of)
-    out = combine.combine(y, L["dst_row"], w)
+    out = combine.combine_exact(y, L["dst_row"], w)
     return {"topk_idx": idx, "topk_w": w, "layout": L, "x_perm": xp, "y": y,
             "out": out, "out_bf16": bf16.round_to_bf16(out)}
 

@@ -89,6 +89,25 @@ def test_combine_worked_example(worked_example, share):
     assert out[:, 0].tolist() == want["combine_y_r_plus_1"]
 
 
+def test_combine_is_the_fp32_slot_order_sum():
+    # products and partial sums are fp32 operations, not fused, not fp64:
+    # slot 0 gives -1; slot 1's product (1 + 2^-23) * (1 + 2^-7) is exactly
+    # 1 + 2^-7 + 2^-23 + 2^-30, rounded in fp32 to 1 + 2^-7 + 2^-23; the sum
+    # is then 2^-7 + 2^-23 (an FMA would keep the 2^-30, fp64 too)
+    w = np.array([[1.0, 1.0 + 2.0 ** -23]])
+    y = np.array([[-1.0], [1.0 + 2.0 ** -7]])
+    dst = np.array([[0, 1]])
+    out = ocombine.combine(y, dst, w)
+    assert out.dtype == np.float32 and out[0, 0] == np.float32(2.0 ** -7 + 2.0 ** -23)
+    assert ocombine.combine_exact(y, dst, w)[0, 0] == 2.0 ** -7 + 2.0 ** -23 + 2.0 ** -30
+    # a rounded product that changes the bf16 result: fp32 gives 2^-23 where
+    # the exact sum is 2^-23 * (1 + 2^-7), itself a bf16 number
+    w = np.array([[1.0 + 2.0 ** -23, 1.0]])
+    y = np.array([[1.0 + 2.0 ** -7], [-(1.0 + 2.0 ** -7)]])
+    assert ocombine.combine_bf16(y, dst, w)[0, 0] == 2.0 ** -23
+    assert bf16.round_to_bf16(ocombine.combine_exact(y, dst, w))[0, 0] == 2.0 ** -23 * (1 + 2.0 ** -7)
+
+
 def test_combine_missing_assignment_raises():
     dst = np.array([[0, 1], [2, -1]])
     with pytest.raises(RuntimeError):
@@ -145,7 +164,7 @@ def test_combine_error_matches_the_pages_benchmark(k, E, default_err):
     idx, w = oroute.route(logits, k)
     L = olayout.layout(idx, E, 1, -1, 1)
     y = bf16.round_to_bf16(rng.standard_normal((L["m_cap"], H)))
-    exact = ocombine.combine(y, L["dst_row"], w)
+    exact = ocombine.combine_exact(y, L["dst_row"], w)
     fused = ocombine.combine_bf16(y, L["dst_row"], w)
     default = ocombine.restore_default(y, L["dst_row"], w)
     rel = lambda a: np.linalg.norm(a - exact) / np.linalg.norm(exact)  # noqa: E731

@@ -19,18 +19,26 @@
 //    consecutive K values of one row of A and one row of B^T, so both
 //    operands are read K-contiguous (weights are stored output-major,
 //    [E, N, K], by the one-time repack).
-//  * Workgroup tile BM x BN (x2 for the gated pair), K staged through LDS in
-//    64-element slices (128-byte rows, 16-byte chunks XOR-swizzled by row so
-//    the MFMA fragment reads spread over the banks), two LDS stages: the
-//    next slice is fetched into registers while the matrix cores work on the
-//    current one.
+//  * 8 wavefronts per workgroup (2 per SIMD), each owning a 64-row block of
+//    accumulators. Workgroup tile: BM rows x BN staged B rows; the gated pair
+//    stages 128 gate + 128 up rows for 128 output columns, so one epilogue
+//    sees both halves of each SwiGLU product.
+//  * Operands go global -> LDS with global_load_lds (16 bytes per lane, no
+//    register staging) through a ring of STAGES K-slices: slice kt+STAGES-1
+//    is in flight while the matrix cores consume slice kt, one barrier per
+//    slice. Each lane picks the global chunk that belongs at its LDS slot,
+//    which realises an XOR swizzle of the 16-byte chunks within a row so the
+//    fragment reads spread over the LDS banks.
 //  * Ragged groups: each workgroup derives the per-expert m-tile prefix from
-//    the device-side counts (no host sync, grid sized for the chip, not for
+//    the device-side counts (no host sync; grid sized for the chip, not for
 //    the routing), then walks tile ids persistently. Ids run expert-major,
 //    then n-tile, then m-tile, and each of the 8 XCDs gets a contiguous range
 //    of ids, so the workgroups sharing a weight tile or an activation tile
 //    sit behind the same L2.
-//  * Rows past an expert's count are zero-filled in LDS and never stored.
+//  * Rows past an expert's count load a valid row of the tile instead (in
+//    bounds; their results are never stored).
+//  * Epilogue through LDS: fp32 -> bf16 (SwiGLU for the gated pair) into a
+//    [BM, OUT_N] tile, then 16-byte row-contiguous stores of the valid rows.
 #include <algorithm>
 
 #include "moe_internal.h"
@@ -38,9 +46,9 @@
 namespace moe {
 namespace {
 
-constexpr int kBK = 64;           // K per LDS stage: 64 bf16 = 128 B per row
-constexpr int kThreads = 256;     // 4 wavefronts, 2 (M) x 2 (N)
 constexpr int kMaxExperts = 1024;
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * kWave;
 
 struct GemmArgs {
   const uint16_t* a;       // [rows, K] bf16
@@ -53,39 +61,74 @@ struct GemmArgs {
   int n, k;
 };
 
-// byte offset of 16-byte chunk `ch` of row `row` in a [rows][64] bf16 stage
-__device__ __forceinline__ int swz(int row, int ch) { return row * 128 + ((ch ^ (row & 7)) << 4); }
+// 16 bytes per lane, global -> LDS, no register staging: lane l's chunk lands
+// at LDS byte lds_addr + 16*l. Issued through inline assembly so that the
+// compiler does not wait for these transfers before unrelated LDS reads; the
+// kernel waits for them itself (s_waitcnt vmcnt + barrier) before reading the
+// stage they fill. The instruction has no register result.
+__device__ __forceinline__ void dma16(const void* base, uint32_t byte_off, uint32_t lds_addr) {
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(byte_off), "s"(base), "{m0}"(lds_addr)
+               : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
 __device__ __forceinline__ float silu(float g) {
   return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
 }
 
-template <int BM, int BN, bool GATED>
-__global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs g) {
-  constexpr int WM = BM / 2, WN = BN / 2;    // wavefront tile
-  constexpr int TM = WM / 32, TN = WN / 32;  // MFMA tiles per wavefront
-  constexpr int NB = GATED ? 2 : 1;          // B operands
-  constexpr int A_LD = BM * kBK / 8 / kThreads;  // 16-byte chunks per thread per stage
-  constexpr int B_LD = BN * kBK / 8 / kThreads;
-  constexpr int A_BYTES = BM * kBK * 2, B_BYTES = BN * kBK * 2;
-  constexpr int STAGE = A_BYTES + NB * B_BYTES;
-  static_assert(A_LD >= 1 && B_LD >= 1, "tile too small for the workgroup");
+// XOR key of a row: which 16-byte chunk slot a logical chunk moves to. The
+// LDS serves a 16-byte-per-lane read 16 lanes (256 bytes, all 64 four-byte
+// banks) at a time, and a fragment read has 16 lanes on 16 consecutive rows
+// at one logical chunk. Those rows must land on 16 distinct 16-byte bank
+// groups: 128-byte rows (BK 64) split them by row parity (32 banks each), so
+// the key takes the next three row bits; 64-byte rows (BK 32) split them by
+// row % 4, so the key takes the next two.
+template <int BK>
+__device__ __forceinline__ int swz_key(int row) {
+  return BK == 64 ? ((row >> 1) & 7) : ((row >> 2) & 3);
+}
 
-  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+template <int BK>
+__device__ __forceinline__ int swz(int row, int ch) {
+  return row * (BK * 2) + ((ch ^ swz_key<BK>(row)) << 4);
+}
+
+template <int BM, int BN, int BK, int STAGES, bool GATED>
+__global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
+  constexpr int WAVES_M = BM / 64, WAVES_N = kWaves / WAVES_M;
+  constexpr int TM = 2;
+  constexpr int OUT_N = GATED ? BN / 2 : BN;  // output columns per tile
+  constexpr int WCOL = OUT_N / WAVES_N;       // output columns per wavefront
+  constexpr int TN = (GATED ? 2 : 1) * WCOL / 32;
+  constexpr int HALF = GATED ? TN / 2 : TN;   // gated: gate tiles j < HALF, up tiles after
+  constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2, STAGE = A_BYTES + B_BYTES;
+  constexpr int A_LOADS = A_BYTES / 1024 / kWaves, B_LOADS = B_BYTES / 1024 / kWaves;
+  constexpr int CPR = BK / 8;           // 16-byte chunks per staged row
+  constexpr int RB = 64 / CPR;          // rows per 1 KiB wave-load
+  constexpr int WAIT = (STAGES - 2) * (A_LOADS + B_LOADS);
+  static_assert(A_LOADS >= 1 && B_LOADS >= 1 && WCOL % 32 == 0 && HALF >= 1, "tile shape");
+  static_assert(STAGE * STAGES >= BM * OUT_N * 2, "epilogue tile must fit the stages");
+  static_assert(!GATED || (B_LOADS % 2 == 0), "gated B loads split evenly");
+
+  __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE];
   __shared__ int mt_prefix[kMaxExperts + 1];
-  __shared__ int wave_tot[kThreads / kWave];
+  __shared__ int wave_tot[kWaves];
 
   const int tid = threadIdx.x, lane = lane_id(), wid = tid / kWave;
-  const int wm = wid / 2, wn = wid % 2;
+  const int wm = wid / WAVES_N, wn = wid % WAVES_N;
   const int K = g.k, N = g.n;
-  const int NT = N / BN, KT = K / kBK;
+  const int NT = N / OUT_N, KT = K / BK;
 
-  // ---- m-tiles per local expert, exclusive prefix (each thread: 4 experts)
+  // m-tiles per local expert, exclusive prefix (each thread: 2 experts)
   {
-    int v[4], run = 0;
+    int v[2], run = 0;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int e = tid * 4 + q;
+    for (int q = 0; q < 2; ++q) {
+      const int e = tid * 2 + q;
       v[q] = e < g.e_loc ? (g.counts[e] + BM - 1) / BM : 0;
       run += v[q];
     }
@@ -101,12 +144,12 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs g) {
     for (int w = 0; w < wid; ++w) before += wave_tot[w];
     int ex = before + incl - run;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int e = tid * 4 + q;
+    for (int q = 0; q < 2; ++q) {
+      const int e = tid * 2 + q;
       if (e < g.e_loc) mt_prefix[e] = ex;
       ex += v[q];
     }
-    if (tid == kThreads - 1) mt_prefix[g.e_loc] = ex;  // grand total
+    if (tid == kThreads - 1) mt_prefix[g.e_loc] = ex;
     __syncthreads();
   }
   const int total = mt_prefix[g.e_loc] * NT;
@@ -115,11 +158,15 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs g) {
   int slot = blockIdx.x;
   if ((G & 7) == 0) slot = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
 
-  // global->LDS assignment: chunk (tid % 8) of rows tid/8 + 32*i
-  const int ld_ch = tid & 7, ld_row = tid >> 3;
+  // this lane's 16-byte chunk inside each 1 KiB wave-load: row l / CPR of the
+  // RB-row block, physical chunk l % CPR, which holds logical chunk
+  // (l % CPR) ^ key(row). The wave-loads of one wavefront start 8*RB rows
+  // apart, which leaves the key unchanged, so one chunk index serves them all.
+  const int ld_r = lane / CPR;
+  const int ld_ch = (lane % CPR) ^ swz_key<BK>(wid * RB + ld_r);
+  const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(smem));
 
   for (int tile = slot; tile < total; tile += G) {
-    // ---- decode tile -> (expert, n-tile, m-tile)
     int lo = 0, hi = g.e_loc - 1;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
@@ -132,110 +179,104 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs g) {
     const int64_t row0 = int64_t(g.offsets[e]) + int64_t(mt) * BM;
     const int rows_valid = min(BM, g.counts[e] - mt * BM);
 
-    const uint16_t* A = g.a + row0 * K;
-    const uint16_t* B0 = g.b0 + (int64_t(e) * N + int64_t(nt) * BN) * K;
-    const uint16_t* B1 = GATED ? g.b1 + (int64_t(e) * N + int64_t(nt) * BN) * K : nullptr;
-
-    u32x4 ra[A_LD], rb0[B_LD], rb1[GATED ? B_LD : 1];
-    auto fetch = [&](int kt) {
-      const int k0 = kt * kBK + ld_ch * 8;
+    // scalar bases + 32-bit per-lane offsets (elements) within the tile
+    const uint16_t* a_base = g.a + row0 * K;
+    const uint16_t* b_base0 = g.b0 + (int64_t(e) * N + int64_t(nt) * OUT_N) * K;
+    const uint16_t* b_base1 = GATED ? g.b1 + (int64_t(e) * N + int64_t(nt) * OUT_N) * K : b_base0;
+    uint32_t oa[A_LOADS], ob[B_LOADS];
 #pragma unroll
-      for (int i = 0; i < A_LD; ++i) {
-        const int r = ld_row + 32 * i;
-        ra[i] = r < rows_valid ? *reinterpret_cast<const u32x4*>(A + int64_t(r) * K + k0)
-                               : u32x4{0u, 0u, 0u, 0u};
-      }
-#pragma unroll
-      for (int i = 0; i < B_LD; ++i) {
-        const int r = ld_row + 32 * i;
-        rb0[i] = *reinterpret_cast<const u32x4*>(B0 + int64_t(r) * K + k0);
-        if constexpr (GATED) rb1[i] = *reinterpret_cast<const u32x4*>(B1 + int64_t(r) * K + k0);
-      }
-    };
-    auto stash = [&](int st) {
-      char* base = smem + st * STAGE;
-#pragma unroll
-      for (int i = 0; i < A_LD; ++i)
-        *reinterpret_cast<u32x4*>(base + swz(ld_row + 32 * i, ld_ch)) = ra[i];
-#pragma unroll
-      for (int i = 0; i < B_LD; ++i) {
-        *reinterpret_cast<u32x4*>(base + A_BYTES + swz(ld_row + 32 * i, ld_ch)) = rb0[i];
-        if constexpr (GATED)
-          *reinterpret_cast<u32x4*>(base + A_BYTES + B_BYTES + swz(ld_row + 32 * i, ld_ch)) =
-              rb1[i];
-      }
-    };
-
-    f32x16 acc[NB][TM][TN];
-#pragma unroll
-    for (int b = 0; b < NB; ++b)
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-#pragma unroll
-          for (int q = 0; q < 16; ++q) acc[b][i][j][q] = 0.f;
-
-    fetch(0);
-    stash(0);
-    __syncthreads();
-
-    for (int kt = 0; kt < KT; ++kt) {
-      const int cur = kt & 1;
-      if (kt + 1 < KT) fetch(kt + 1);
-      const char* base = smem + cur * STAGE;
-#pragma unroll
-      for (int kk = 0; kk < kBK / 16; ++kk) {
-        const int ch = 2 * kk + (lane >> 5);
-        bf16x8 af[TM], bf[NB][TN];
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-          af[i] = *reinterpret_cast<const bf16x8*>(base + swz(wm * WM + i * 32 + (lane & 31), ch));
-#pragma unroll
-        for (int b = 0; b < NB; ++b)
-#pragma unroll
-          for (int j = 0; j < TN; ++j)
-            bf[b][j] = *reinterpret_cast<const bf16x8*>(
-                base + A_BYTES + b * B_BYTES + swz(wn * WN + j * 32 + (lane & 31), ch));
-#pragma unroll
-        for (int b = 0; b < NB; ++b)
-#pragma unroll
-          for (int i = 0; i < TM; ++i)
-#pragma unroll
-            for (int j = 0; j < TN; ++j)
-              acc[b][i][j] =
-                  __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[b][j], acc[b][i][j], 0, 0, 0);
-      }
-      if (kt + 1 < KT) stash(cur ^ 1);
-      __syncthreads();
+    for (int i = 0; i < A_LOADS; ++i) {
+      const int r = (wid + kWaves * i) * RB + ld_r;
+      oa[i] = uint32_t(min(r, rows_valid - 1)) * uint32_t(K) + ld_ch * 8;
     }
+#pragma unroll
+    for (int i = 0; i < B_LOADS; ++i) {
+      const int r = (wid + kWaves * i) * RB + ld_r;  // gated: first half gate rows, then up
+      ob[i] = uint32_t(GATED ? r % (BN / 2) : r) * uint32_t(K) + ld_ch * 8;
+    }
+    auto issue = [&](int kt, int st) {
+      const uint32_t sbase = lds0 + st * STAGE;
+      const uint32_t k0 = uint32_t(kt) * BK;
+#pragma unroll
+      for (int i = 0; i < A_LOADS; ++i)
+        dma16(a_base, (oa[i] + k0) * 2, sbase + (wid + kWaves * i) * 1024);
+#pragma unroll
+      for (int i = 0; i < B_LOADS; ++i) {
+        const uint16_t* bb = (GATED && i >= B_LOADS / 2) ? b_base1 : b_base0;
+        dma16(bb, (ob[i] + k0) * 2, sbase + A_BYTES + (wid + kWaves * i) * 1024);
+      }
+    };
 
-    // ---- epilogue: lane holds column (lane % 32), rows 8*(q/4) + 4*(lane/32) + q%4
-    uint16_t* C = g.c + row0 * N + int64_t(nt) * BN;
+    f32x16 acc[TM][TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j)
 #pragma unroll
-        for (int q = 0; q < 16; ++q) {
-          const int r = wm * WM + i * 32 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
-          const int col = wn * WN + j * 32 + (lane & 31);
-          if (r < rows_valid) {
-            float v = acc[0][i][j][q];
-            if constexpr (GATED) v = silu(v) * acc[NB - 1][i][j][q];
-            C[int64_t(r) * N + col] = to_bf16(v);
-          }
+        for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+
+#pragma unroll
+    for (int s = 0; s < STAGES - 1; ++s)
+      if (s < KT) issue(s, s);
+    for (int kt = 0; kt < KT; ++kt) {
+      if (kt + STAGES - 2 < KT) wait_vmcnt<WAIT>(); else wait_vmcnt<0>();
+      __syncthreads();  // slice kt visible to all; everyone is done with slice kt-1
+      if (kt + STAGES - 1 < KT) issue(kt + STAGES - 1, (kt + STAGES - 1) % STAGES);
+      const char* base = smem + (kt % STAGES) * STAGE;
+#pragma unroll
+      for (int kk = 0; kk < BK / 16; ++kk) {
+        const int ch = 2 * kk + (lane >> 5);
+        bf16x8 af[TM], bf[TN];
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+          af[i] = *reinterpret_cast<const bf16x8*>(
+              base + swz<BK>(wm * 64 + i * 32 + (lane & 31), ch));
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const int brow = GATED ? (j / HALF) * (BN / 2) + wn * WCOL + (j % HALF) * 32
+                                 : wn * WCOL + j * 32;
+          bf[j] = *reinterpret_cast<const bf16x8*>(base + A_BYTES +
+                                                   swz<BK>(brow + (lane & 31), ch));
         }
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+      }
+    }
+    __syncthreads();  // every wavefront is done reading the last slice
+
+    // accumulators (lane: column lane % 32, rows 8*(q/4) + 4*(lane/32) + q%4)
+    // -> bf16 tile in LDS -> 16-byte stores of the valid rows
+    uint16_t* ct = reinterpret_cast<uint16_t*>(smem);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < HALF; ++j)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          const int r = wm * 64 + i * 32 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
+          const int col = wn * WCOL + j * 32 + (lane & 31);
+          float v = acc[i][j][q];
+          if constexpr (GATED) v = silu(v) * acc[i][j + HALF][q];
+          ct[r * OUT_N + col] = to_bf16(v);
+        }
+    __syncthreads();
+    constexpr int OCH = OUT_N / 8;  // 16-byte chunks per output row
+    uint16_t* C = g.c + row0 * N + int64_t(nt) * OUT_N;
+    for (int c = tid; c < rows_valid * OCH; c += kThreads) {
+      const int r = c / OCH, ch = c % OCH;
+      *reinterpret_cast<u32x4*>(C + int64_t(r) * N + ch * 8) =
+          *reinterpret_cast<const u32x4*>(ct + r * OUT_N + ch * 8);
+    }
+    __syncthreads();  // the tile buffer is read out before the next tile's loads
   }
 }
 
-template <int BM, int BN, bool GATED>
-hipError_t launch_grouped(const GemmArgs& a, hipStream_t s) {
-  // workgroups per CU that fit in LDS (160 KiB per CU on gfx950)
-  constexpr int lds = 2 * (BM * kBK * 2 + (GATED ? 2 : 1) * BN * kBK * 2) + 4 * (kMaxExperts + 5);
-  const int per_cu = std::max(1, std::min(2, (160 * 1024) / lds));
-  const int grid = device_cu_count() * per_cu;
-  grouped_gemm_kernel<BM, BN, GATED><<<grid, kThreads, 0, s>>>(a);
+template <int BM, int BN, int BK, int STAGES, bool GATED>
+hipError_t launch(const GemmArgs& a, hipStream_t s) {
+  grouped_gemm_kernel<BM, BN, BK, STAGES, GATED><<<device_cu_count(), kThreads, 0, s>>>(a);
   return hipGetLastError();
 }
 
@@ -245,18 +286,19 @@ hipError_t launch_gate_up(const void* x_perm, const int32_t* offsets, const int3
                           int e_loc, int64_t m_cap, int H, int I, const void* w1t,
                           const void* w3t, void* h, hipStream_t s) {
   (void)m_cap;
-  GemmArgs a{static_cast<const uint16_t*>(x_perm), static_cast<const uint16_t*>(w1t),
-             static_cast<const uint16_t*>(w3t), static_cast<uint16_t*>(h), offsets, counts,
-             e_loc, I, H};
-  return launch_grouped<128, 128, true>(a, s);
+  const GemmArgs a{static_cast<const uint16_t*>(x_perm), static_cast<const uint16_t*>(w1t),
+                   static_cast<const uint16_t*>(w3t), static_cast<uint16_t*>(h), offsets, counts,
+                   e_loc, I, H};
+  return launch<256, 256, 64, 2, true>(a, s);  // I % 128 == 0: 128 output columns per tile
 }
 
 hipError_t launch_down(const void* h, const int32_t* offsets, const int32_t* counts, int e_loc,
                        int64_t m_cap, int I, int H, const void* w2t, void* y, hipStream_t s) {
   (void)m_cap;
-  GemmArgs a{static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(w2t), nullptr,
-             static_cast<uint16_t*>(y), offsets, counts, e_loc, H, I};
-  return launch_grouped<128, 128, false>(a, s);
+  const GemmArgs a{static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(w2t), nullptr,
+                   static_cast<uint16_t*>(y), offsets, counts, e_loc, H, I};
+  if (H % 256 == 0) return launch<256, 256, 64, 2, false>(a, s);
+  return launch<256, 128, 64, 2, false>(a, s);
 }
 
 }  // namespace moe

@@ -23,8 +23,8 @@
 //    accumulators. Workgroup tile: BM rows x BN staged B rows; the gated pair
 //    stages 128 gate + 128 up rows for 128 output columns, so one epilogue
 //    sees both halves of each SwiGLU product.
-//  * Operands go global -> LDS with global_load_lds (16 bytes per lane, no
-//    register staging) through a ring of STAGES K-slices: slice kt+STAGES-1
+//  * Operands go memory -> LDS with buffer_load ... lds (16 bytes per lane,
+//    no register staging) through a ring of STAGES K-slices: slice kt+STAGES-1
 //    is in flight while the matrix cores consume slice kt, one barrier per
 //    slice. Each lane picks the global chunk that belongs at its LDS slot,
 //    which realises an XOR swizzle of the 16-byte chunks within a row so the
@@ -35,11 +35,12 @@
 //    then n-tile, then m-tile, and each of the 8 XCDs gets a contiguous range
 //    of ids, so the workgroups sharing a weight tile or an activation tile
 //    sit behind the same L2.
-//  * Rows past an expert's count load a valid row of the tile instead (in
-//    bounds; their results are never stored).
+//  * Each tile's A range ends at its expert's last row: the rows past it
+//    read as zeros through the buffer bound (their results are never stored).
 //  * Epilogue through LDS: fp32 -> bf16 (SwiGLU for the gated pair) into a
 //    [BM, OUT_N] tile, then 16-byte row-contiguous stores of the valid rows.
 #include <algorithm>
+#include <type_traits>
 
 #include "moe_internal.h"
 
@@ -61,13 +62,29 @@ struct GemmArgs {
   int n, k;
 };
 
-// 16 bytes per lane, global -> LDS, no register staging: lane l's chunk lands
-// at LDS byte lds_addr + 16*l. Issued through inline assembly so that the
-// compiler does not wait for these transfers before unrelated LDS reads; the
-// kernel waits for them itself (s_waitcnt vmcnt + barrier) before reading the
-// stage they fill. The instruction has no register result.
-__device__ __forceinline__ void dma16(const void* base, uint32_t byte_off, uint32_t lds_addr) {
-  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(byte_off), "s"(base), "{m0}"(lds_addr)
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer resource for a raw byte range [base, base + bytes): loads past the
+// end return zeros instead of touching memory.
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane(static_cast<int>(a & 0xffffffffu));
+  r[1] = __builtin_amdgcn_readfirstlane(static_cast<int>((a >> 32) & 0xffffu));  // stride 0
+  r[2] = __builtin_amdgcn_readfirstlane(static_cast<int>(bytes));               // num_records
+  r[3] = 0x00020000;  // raw 32-bit data format, no swizzle
+  return r;
+}
+
+// 16 bytes per lane, memory -> LDS through the buffer path, no register
+// staging: lane l's chunk lands at LDS byte lds_addr + 16*l. Issued through
+// inline assembly so that the compiler does not wait for these transfers
+// before unrelated LDS reads; the kernel waits for them itself (s_waitcnt
+// vmcnt + barrier) before reading the stage they fill. The instruction has
+// no register result.
+__device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t byte_off, uint32_t lds_addr) {
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(byte_off), "s"(rsrc),
+               "{m0}"(lds_addr)
                : "memory");
 }
 
@@ -152,7 +169,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
     if (tid == kThreads - 1) mt_prefix[g.e_loc] = ex;
     __syncthreads();
   }
-  const int total = mt_prefix[g.e_loc] * NT;
+  const int total = uniform(mt_prefix[g.e_loc]) * NT;
 
   const int G = gridDim.x;
   int slot = blockIdx.x;
@@ -172,22 +189,28 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
       const int mid = (lo + hi + 1) >> 1;
       if (mt_prefix[mid] * NT <= tile) lo = mid; else hi = mid - 1;
     }
-    const int e = lo;
-    const int mtiles = mt_prefix[e + 1] - mt_prefix[e];
-    const int rem = tile - mt_prefix[e] * NT;
+    // tile coordinates are the same in every lane: keep them in scalar registers
+    const int e = uniform(lo);
+    const int mtiles = uniform(mt_prefix[e + 1] - mt_prefix[e]);
+    const int rem = tile - uniform(mt_prefix[e]) * NT;
     const int nt = rem / mtiles, mt = rem % mtiles;
-    const int64_t row0 = int64_t(g.offsets[e]) + int64_t(mt) * BM;
-    const int rows_valid = min(BM, g.counts[e] - mt * BM);
+    const int64_t row0 = int64_t(uniform(g.offsets[e])) + int64_t(mt) * BM;
+    const int rows_valid = min(BM, uniform(g.counts[e]) - mt * BM);
 
     // scalar bases + 32-bit per-lane offsets (elements) within the tile
     const uint16_t* a_base = g.a + row0 * K;
     const uint16_t* b_base0 = g.b0 + (int64_t(e) * N + int64_t(nt) * OUT_N) * K;
     const uint16_t* b_base1 = GATED ? g.b1 + (int64_t(e) * N + int64_t(nt) * OUT_N) * K : b_base0;
+    // A's range ends at the expert's last valid row of the tile: the rows
+    // past it read as zeros (their results are never stored)
+    const i32x4 ra = make_rsrc(a_base, uint32_t(rows_valid) * uint32_t(K) * 2u);
+    const i32x4 rb0 = make_rsrc(b_base0, uint32_t(OUT_N) * uint32_t(K) * 2u);
+    const i32x4 rb1 = make_rsrc(b_base1, uint32_t(OUT_N) * uint32_t(K) * 2u);
     uint32_t oa[A_LOADS], ob[B_LOADS];
 #pragma unroll
     for (int i = 0; i < A_LOADS; ++i) {
       const int r = (wid + kWaves * i) * RB + ld_r;
-      oa[i] = uint32_t(min(r, rows_valid - 1)) * uint32_t(K) + ld_ch * 8;
+      oa[i] = uint32_t(r) * uint32_t(K) + ld_ch * 8;
     }
 #pragma unroll
     for (int i = 0; i < B_LOADS; ++i) {
@@ -199,12 +222,11 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
       const uint32_t k0 = uint32_t(kt) * BK;
 #pragma unroll
       for (int i = 0; i < A_LOADS; ++i)
-        dma16(a_base, (oa[i] + k0) * 2, sbase + (wid + kWaves * i) * 1024);
+        dma16(ra, (oa[i] + k0) * 2, sbase + (wid + kWaves * i) * 1024);
 #pragma unroll
-      for (int i = 0; i < B_LOADS; ++i) {
-        const uint16_t* bb = (GATED && i >= B_LOADS / 2) ? b_base1 : b_base0;
-        dma16(bb, (ob[i] + k0) * 2, sbase + A_BYTES + (wid + kWaves * i) * 1024);
-      }
+      for (int i = 0; i < B_LOADS; ++i)
+        dma16((GATED && i >= B_LOADS / 2) ? rb1 : rb0, (ob[i] + k0) * 2,
+              sbase + A_BYTES + (wid + kWaves * i) * 1024);
     };
 
     f32x16 acc[TM][TN];
@@ -215,35 +237,70 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
 #pragma unroll
         for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
 
-#pragma unroll
-    for (int s = 0; s < STAGES - 1; ++s)
-      if (s < KT) issue(s, s);
-    for (int kt = 0; kt < KT; ++kt) {
-      if (kt + STAGES - 2 < KT) wait_vmcnt<WAIT>(); else wait_vmcnt<0>();
-      __syncthreads();  // slice kt visible to all; everyone is done with slice kt-1
-      if (kt + STAGES - 1 < KT) issue(kt + STAGES - 1, (kt + STAGES - 1) % STAGES);
-      const char* base = smem + (kt % STAGES) * STAGE;
-#pragma unroll
-      for (int kk = 0; kk < BK / 16; ++kk) {
+    // 32-row blocks of this wavefront that hold valid rows (0..TM): a partly
+    // filled tile skips the matrix work (and A reads) of its empty blocks
+    const int nblk = uniform(min(TM, max(0, (rows_valid - wm * 64 + 31) / 32)));
+
+    constexpr int KK = BK / 16;
+    // The K loop for NB (compile-time) valid 32-row blocks, software-pipelined
+    // around its one barrier per slice: the fragments of a slice's last
+    // 16-wide step are read before the barrier, so those MFMAs run while the
+    // first reads of the next slice are in flight. Every variant executes the
+    // same loads and barriers; only the matrix work differs.
+    auto kloop = [&](auto nb_tag) {
+      constexpr int NB = decltype(nb_tag)::value;
+      bf16x8 fa[2][TM], fb[2][TN];
+      auto read_frags = [&](const char* base, int kk, bf16x8 (&a)[TM], bf16x8 (&b)[TN]) {
         const int ch = 2 * kk + (lane >> 5);
-        bf16x8 af[TM], bf[TN];
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
-          af[i] = *reinterpret_cast<const bf16x8*>(
+        for (int i = 0; i < NB; ++i)
+          a[i] = *reinterpret_cast<const bf16x8*>(
               base + swz<BK>(wm * 64 + i * 32 + (lane & 31), ch));
+        if (NB == 0) return;
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
           const int brow = GATED ? (j / HALF) * (BN / 2) + wn * WCOL + (j % HALF) * 32
                                  : wn * WCOL + j * 32;
-          bf[j] = *reinterpret_cast<const bf16x8*>(base + A_BYTES +
-                                                   swz<BK>(brow + (lane & 31), ch));
+          b[j] = *reinterpret_cast<const bf16x8*>(base + A_BYTES +
+                                                  swz<BK>(brow + (lane & 31), ch));
         }
+      };
+      auto mfma = [&](const bf16x8 (&a)[TM], const bf16x8 (&b)[TN]) {
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
+        for (int i = 0; i < NB; ++i)
 #pragma unroll
           for (int j = 0; j < TN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+      };
+
+#pragma unroll
+      for (int s = 0; s < STAGES - 1; ++s)
+        if (s < KT) issue(s, s);
+      if (STAGES - 2 < KT) wait_vmcnt<WAIT>(); else wait_vmcnt<0>();
+      __syncthreads();  // slice 0 visible
+      if (STAGES - 1 < KT) issue(STAGES - 1, STAGES - 1);
+      read_frags(smem, 0, fa[0], fb[0]);
+      for (int kt = 0; kt < KT; ++kt) {
+        const char* base = smem + (kt % STAGES) * STAGE;
+#pragma unroll
+        for (int kk = 0; kk + 1 < KK; ++kk) {
+          read_frags(base, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
+          mfma(fa[kk & 1], fb[kk & 1]);
+        }
+        if (kt + 1 < KT) {
+          // slice kt+1 landed (this wavefront's part), and all of slice kt is read
+          if (kt + STAGES - 1 < KT) wait_vmcnt<WAIT>(); else wait_vmcnt<0>();
+          __syncthreads();
+          if (kt + STAGES < KT) issue(kt + STAGES, (kt + STAGES) % STAGES);
+          read_frags(smem + ((kt + 1) % STAGES) * STAGE, 0, fa[0], fb[0]);
+        }
+        mfma(fa[(KK - 1) & 1], fb[(KK - 1) & 1]);
       }
+    };
+    switch (nblk) {
+      case TM: kloop(std::integral_constant<int, TM>{}); break;
+      case 1: kloop(std::integral_constant<int, 1>{}); break;
+      default: kloop(std::integral_constant<int, 0>{}); break;
     }
     __syncthreads();  // every wavefront is done reading the last slice
 

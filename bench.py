@@ -1,6 +1,6 @@
 """MoE-layer throughput on one MI355X.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload mixtral_8x7b] [--dist ...]
+    python bench.py [--gpus 1] [--steps 30] [--warmup 30] [--workload mixtral_8x7b] [--dist ...]
 
 One step = one pass of the whole single-GPU layer over one batch of seeded
 synthetic input already resident in HBM:
@@ -38,15 +38,32 @@ def log(*a):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default="mixtral_8x7b")
     ap.add_argument("--dist", default=None)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for the CPU baseline sample")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB five times (the reference "
+                         "kernel for scaling rocprofv3 FETCH_SIZE/WRITE_SIZE readings) and exit")
     return ap.parse_args()
+
+
+def calibrate_copy(mib: int):
+    """A plain device-to-device copy of known size: its FETCH_SIZE and WRITE_SIZE
+    readings (KiB per dispatch) against the true mib*1024 KiB give the factor that
+    turns the counters into HBM bytes."""
+    import torch
+    n = mib * (1 << 20)
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes": n, "launches": 5}), flush=True)
 
 
 def traffic_record(kernel: str, workload: str):
@@ -128,6 +145,9 @@ def cpu_baseline(cfg, dist, layer_args, budget_s):
 
 def main():
     args = parse()
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
     if args.gpus != 1:
         print(f"bench.py runs one GPU only (got --gpus {args.gpus}): this build measures one "
               "GPU's share of the layer; sharding across GPUs is not implemented.",
@@ -153,10 +173,16 @@ def main():
     stages = layer.stages(x, logits)
     stream = torch.cuda.current_stream(dev)
 
-    for _ in range(args.warmup):
+    wev = [torch.cuda.Event(enable_timing=True) for _ in range(args.warmup + 1)]
+    wev[0].record(stream)
+    for w in range(args.warmup):
         for _, run in stages:
             run()
+        wev[w + 1].record(stream)
     torch.cuda.synchronize()
+    if args.warmup:
+        ws = [wev[i].elapsed_time(wev[i + 1]) for i in range(args.warmup)]
+        log("warmup step ms: first %.3f, last %.3f, min %.3f" % (ws[0], ws[-1], min(ws)))
 
     # algorithmic work of this batch (read once, outside the timed region)
     counts = layer.L.local_counts.cpu().numpy().astype(np.int64)

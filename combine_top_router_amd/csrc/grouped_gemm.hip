@@ -34,7 +34,9 @@
 //    the routing), then walks tile ids persistently. Ids run expert-major,
 //    then n-tile, then m-tile, and each of the 8 XCDs gets a contiguous range
 //    of ids, so the workgroups sharing a weight tile or an activation tile
-//    sit behind the same L2.
+//    sit behind the same L2. An expert's c rows form ceil(c/BM) tiles of
+//    equal height, so no tile is a short tail that would finish early and
+//    pull its workgroup out of step with the others sharing its data.
 //  * Each tile's A range ends at its expert's last row: the rows past it
 //    read as zeros through the buffer bound (their results are never stored).
 //  * Epilogue through LDS: fp32 -> bf16 (SwiGLU for the gated pair) into a
@@ -194,8 +196,13 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
     const int mtiles = uniform(mt_prefix[e + 1] - mt_prefix[e]);
     const int rem = tile - uniform(mt_prefix[e]) * NT;
     const int nt = rem / mtiles, mt = rem % mtiles;
-    const int64_t row0 = int64_t(uniform(g.offsets[e])) + int64_t(mt) * BM;
-    const int rows_valid = min(BM, uniform(g.counts[e]) - mt * BM);
+    // the expert's rows split into mtiles tiles of equal height (a multiple
+    // of 32, at most BM): no short tail tile, so the workgroups that share
+    // weight and activation tiles through L2 take equally long and stay in step
+    const int cnt_e = uniform(g.counts[e]);
+    const int hgt = ((cnt_e + mtiles - 1) / mtiles + 31) / 32 * 32;
+    const int64_t row0 = int64_t(uniform(g.offsets[e])) + int64_t(mt) * hgt;
+    const int rows_valid = min(hgt, cnt_e - mt * hgt);
 
     // scalar bases + 32-bit per-lane offsets (elements) within the tile
     const uint16_t* a_base = g.a + row0 * K;

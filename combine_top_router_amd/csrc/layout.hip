@@ -12,7 +12,9 @@
 // text, section "Attribution"); rows are named by the flat index
 // token*top_k + slot (DeepSpeed PR #8847, section "Change").
 //
-// Three kernels on one stream:
+// Up to 4096 assignments one workgroup does everything in one launch (see
+// layout_fused_kernel): one CU is then as fast as the whole chip and two
+// launches are saved. Beyond that, three kernels on one stream:
 //   count   one workgroup per tile of flat assignments (tiles never cross a
 //           source-rank boundary): LDS histogram over all experts.
 //   scan    one workgroup: per-rank and per-expert totals, split matrix,
@@ -240,7 +242,7 @@ __global__ __launch_bounds__(kThreads) void layout_scatter_kernel(
         const int64_t row = int64_t(offsets[el]) + tile_base[size_t(b) * el_n + el] +
                             wbase[w * el_n + el] + pre[r];
         dst_row[i] = static_cast<int32_t>(row);
-        if (row < m_cap) src_row[row] = static_cast<int32_t>(i);
+        if (row >= 0 && row < m_cap) src_row[row] = static_cast<int32_t>(i);
       } else {
         dst_row[i] = -1;
       }
@@ -256,6 +258,172 @@ __global__ __launch_bounds__(kThreads) void layout_scatter_kernel(
   for (int64_t r = int64_t(offsets[el_n]) + int64_t(b) * kThreads + threadIdx.x; r < m_cap;
        r += int64_t(gridDim.x) * kThreads)
     src_row[r] = -1;
+}
+
+// ---------------------------------------------------------------------------
+// Single-workgroup layout for up to kFusedMaxN assignments: one launch does
+// the histogram, the scan and the scatter. 16 wavefronts each own a
+// contiguous segment of flat assignments. Pass 1 builds the per-(source
+// rank, expert) histogram with LDS atomics and each wavefront's count per
+// local expert with ballots; pass 2 turns them into totals, splits, padded
+// offsets and each wavefront's first row per local expert; pass 3 re-reads
+// the segment and assigns rows in flat-index order (ballot rank + the
+// wavefront's running row), so the order is the same stable order as the
+// tiled path.
+constexpr int kFusedThreads = 1024, kFusedWaves = kFusedThreads / kWave;
+constexpr int kFusedMaxN = 4096;  // beyond this the tiled path is faster
+constexpr int kFusedMaxHist = 16384, kFusedMaxLocal = 1024;
+constexpr int kFusedBatch = 8;
+
+__device__ __forceinline__ uint64_t match_mask(int key, int bits, bool valid) {
+  uint64_t m = __ballot(valid);
+  for (int bit = 0; bit < bits; ++bit) {
+    const bool set = (key >> bit) & 1;
+    const uint64_t bb = __ballot(set);
+    m &= set ? bb : ~bb;
+  }
+  return m;
+}
+
+__global__ __launch_bounds__(kFusedThreads) void layout_fused_kernel(
+    LayoutPlan p, const int32_t* __restrict__ idx, int32_t* __restrict__ expert_counts,
+    int32_t* __restrict__ send_counts, int32_t* __restrict__ split_matrix,
+    int32_t* __restrict__ recv_counts, int32_t* __restrict__ output_splits,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ dst_row, int32_t* __restrict__ src_row,
+    int64_t m_cap) {
+  __shared__ int32_t hist[kFusedMaxHist];                  // [ep, E]
+  __shared__ int32_t wcnt[kFusedWaves * kFusedMaxLocal];   // [wave, e_loc]
+  __shared__ int32_t lcnt[kFusedMaxLocal];
+  __shared__ int32_t off[kFusedMaxLocal + 1];
+  __shared__ int32_t wave_tot[kFusedWaves];
+  const int tid = threadIdx.x, w = tid / kWave, lane = lane_id();
+  const int el_n = p.e_loc, E = p.E;
+  const int64_t N = p.T * p.k;
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+
+  for (int q = tid; q < p.ep * E; q += kFusedThreads) hist[q] = 0;
+  for (int q = tid; q < kFusedWaves * el_n; q += kFusedThreads) wcnt[q] = 0;
+  __syncthreads();
+
+  const int64_t seg = ((N + kFusedWaves - 1) / kFusedWaves + kWave - 1) / kWave * kWave;
+  const int64_t s0 = int64_t(w) * seg, s1 = min(s0 + seg, N);
+  int32_t* mycnt = wcnt + w * el_n;
+  const uint32_t chunk32 = static_cast<uint32_t>(p.chunk);  // N < 2^31 on this path
+
+  // pass 1: histograms. kBatch loads per lane are issued before any is used,
+  // so a wavefront waits for one memory latency per kBatch*64 assignments.
+  for (int64_t base = s0; base < s1; base += kWave * kFusedBatch) {
+    int ev[kFusedBatch];
+#pragma unroll
+    for (int v = 0; v < kFusedBatch; ++v) {
+      const int64_t i = base + v * kWave + lane;
+      ev[v] = i < s1 ? idx[i] : -1;
+    }
+#pragma unroll
+    for (int v = 0; v < kFusedBatch; ++v) {
+      const int64_t i = base + v * kWave + lane;
+      const bool valid = i < s1;
+      const int e = ev[v];
+      if (valid && static_cast<unsigned>(e) < static_cast<unsigned>(E))
+        atomicAdd(&hist[int(uint32_t(i) / chunk32) * E + e], 1);
+      const int el = (e >= p.first && e < p.first + el_n) ? e - p.first : el_n;
+      const uint64_t m = match_mask(el, p.key_bits, valid);
+      if (el < el_n && __popcll(m & below) == 0) mycnt[el] += __popcll(m);
+    }
+  }
+  __syncthreads();
+
+  // pass 2: totals, split plan, padded offsets, first row of each wavefront
+  for (int e = tid; e < E; e += kFusedThreads) {
+    int total = 0;
+    for (int s = 0; s < p.ep; ++s) {
+      const int c = hist[s * E + e];
+      if (send_counts) send_counts[s * E + e] = c;
+      total += c;
+    }
+    if (expert_counts) expert_counts[e] = total;
+  }
+  for (int el = tid; el < el_n; el += kFusedThreads) {
+    int total = 0;
+    for (int q = 0; q < kFusedWaves; ++q) total += wcnt[q * el_n + el];
+    lcnt[el] = total;
+  }
+  if (recv_counts)
+    for (int q = tid; q < p.ep * el_n; q += kFusedThreads)
+      recv_counts[q] = hist[(q / el_n) * E + p.first + q % el_n];
+  if (output_splits)
+    for (int s = tid; s < p.ep; s += kFusedThreads) {
+      int sum = 0;
+      for (int el = 0; el < el_n; ++el) sum += hist[s * E + p.first + el];
+      output_splits[s] = sum;
+    }
+  if (split_matrix) {
+    const int eper = E / p.ep;
+    for (int q = tid; q < p.ep * p.ep; q += kFusedThreads) {
+      const int s = q / p.ep, d = q % p.ep;
+      int sum = 0;
+      for (int e = 0; e < eper; ++e) sum += hist[s * E + d * eper + e];
+      split_matrix[q] = sum;
+    }
+  }
+  __syncthreads();
+  {
+    const int padded = tid < el_n ? (lcnt[tid] + p.align - 1) / p.align * p.align : 0;
+    const int incl = block_inclusive_scan_1024(padded, wave_tot);
+    if (tid == 0) {
+      off[0] = 0;
+      offsets[0] = 0;
+    }
+    if (tid < el_n) {
+      off[tid + 1] = incl;
+      offsets[tid + 1] = incl;
+    }
+  }
+  __syncthreads();
+  for (int el = tid; el < el_n; el += kFusedThreads) {
+    int run = off[el];
+    for (int q = 0; q < kFusedWaves; ++q) {
+      const int c = wcnt[q * el_n + el];
+      wcnt[q * el_n + el] = run;
+      run += c;
+    }
+  }
+  __syncthreads();
+
+  // pass 3: rows in flat-index order (chunks of 64 in order within a batch)
+  for (int64_t base = s0; base < s1; base += kWave * kFusedBatch) {
+    int ev[kFusedBatch];
+#pragma unroll
+    for (int v = 0; v < kFusedBatch; ++v) {
+      const int64_t i = base + v * kWave + lane;
+      ev[v] = i < s1 ? idx[i] : -1;
+    }
+#pragma unroll
+    for (int v = 0; v < kFusedBatch; ++v) {
+      const int64_t i = base + v * kWave + lane;
+      const bool valid = i < s1;
+      const int e = ev[v];
+      const int el = (e >= p.first && e < p.first + el_n) ? e - p.first : el_n;
+      const uint64_t m = match_mask(el, p.key_bits, valid);
+      if (el < el_n) {
+        const int old = mycnt[el];
+        const int rank = __popcll(m & below);
+        const int row = old + rank;
+        if (rank == 0) mycnt[el] = old + __popcll(m);
+        dst_row[i] = row;
+        if (row >= 0 && row < m_cap) src_row[row] = static_cast<int32_t>(i);
+      } else if (valid) {
+        dst_row[i] = -1;
+      }
+    }
+  }
+
+  // padding rows of each local expert and the tail up to m_cap: -1
+  for (int el = w; el < el_n; el += kFusedWaves) {
+    const int64_t hi = min(int64_t(off[el + 1]), m_cap);
+    for (int64_t r = int64_t(off[el]) + lcnt[el] + lane; r < hi; r += kWave) src_row[r] = -1;
+  }
+  for (int64_t r = int64_t(off[el_n]) + tid; r < m_cap; r += kFusedThreads) src_row[r] = -1;
 }
 
 }  // namespace
@@ -292,6 +460,13 @@ hipError_t launch_layout(const LayoutPlan& p, const int32_t* topk_idx, int32_t* 
                          int32_t* send_counts, int32_t* split_matrix, int32_t* recv_counts,
                          int32_t* output_splits, int32_t* offsets, int32_t* dst_row,
                          int32_t* src_row, int64_t m_cap, void* ws_base, hipStream_t s) {
+  if (p.T * p.k <= kFusedMaxN && int64_t(p.ep) * p.E <= kFusedMaxHist &&
+      p.e_loc <= kFusedMaxLocal) {
+    layout_fused_kernel<<<1, kFusedThreads, 0, s>>>(p, topk_idx, expert_counts, send_counts,
+                                                    split_matrix, recv_counts, output_splits,
+                                                    offsets, dst_row, src_row, m_cap);
+    return hipGetLastError();
+  }
   const Ws ws = carve(p, ws_base);
   if (p.num_tiles > 0) {
     layout_count_kernel<<<p.num_tiles, kThreads, sizeof(int32_t) * p.E, s>>>(p, topk_idx,

@@ -1,4 +1,4 @@
-// Token-choice top-k routing: one wavefront per token.
+// Token-choice top-k routing.
 //
 // Selection follows the token-choice top-k router of the AutoEP runtime
 // (DeepSpeed AutoEP commit text, section "Attribution": ep_router.py after
@@ -8,9 +8,13 @@
 // softmax of the k selected logits; kept in fp32, the router dtype
 // (DeepSpeed PR #8847, section "Change").
 //
-// Each lane holds up to VPL logits (expert ids lane, lane+64, ...) as 64-bit
-// keys whose order is (logit descending, id ascending); k rounds of a wave
-// max pick the winners. HBM-bound: T*E*4 bytes in, T*k*8 out.
+// A group of G lanes (8, 16 or 32) owns one token, so a wavefront routes 64/G
+// tokens at once; lane j of the group holds the VPL consecutive logits of
+// experts j*VPL .. j*VPL+VPL-1 (one contiguous load per lane) as 64-bit keys
+// whose order is (logit descending, id ascending). Each of the k rounds takes
+// the lane's best key, a log2(G)-step xor-shuffle max inside the group, and
+// retires the winner; lane j keeps the j-th winner. HBM-bound: T*E*4 bytes
+// in, T*k*8 out.
 #include "moe_internal.h"
 
 namespace moe {
@@ -35,61 +39,81 @@ __device__ __forceinline__ uint64_t make_key(float f, int e) {
   return (static_cast<uint64_t>(ordered_bits(f)) << 32) | static_cast<uint32_t>(~e);
 }
 
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+template <int G>
+__device__ __forceinline__ uint64_t group_max_u64(uint64_t v) {
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    uint32_t lo = __shfl_xor(static_cast<uint32_t>(v), off, kWave);
-    uint32_t hi = __shfl_xor(static_cast<uint32_t>(v >> 32), off, kWave);
-    uint64_t o = (static_cast<uint64_t>(hi) << 32) | lo;
+  for (int off = G / 2; off >= 1; off >>= 1) {
+    const uint32_t lo = __shfl_xor(static_cast<uint32_t>(v), off, kWave);
+    const uint32_t hi = __shfl_xor(static_cast<uint32_t>(v >> 32), off, kWave);
+    const uint64_t o = (static_cast<uint64_t>(hi) << 32) | lo;
     v = o > v ? o : v;
   }
   return v;
 }
 
-template <int VPL>
+template <int G, int VPL>
 __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ logits, int64_t T,
                                                     int E, int k, int32_t* __restrict__ idx_out,
                                                     float* __restrict__ w_out) {
-  const int64_t t = uniform(static_cast<int64_t>(blockIdx.x) * 4 + threadIdx.x / kWave);
-  if (t >= T) return;
-  const int lane = lane_id();
-  const float* row = logits + t * E;
+  const int64_t t = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) / G;
+  const int j = threadIdx.x % G;  // lane within the token's group
+  // every lane of a group shares t; groups past T still run the shuffles
+  // (they are all in the same wavefront) but load and store nothing
+  const bool live = t < T;
+  const float* row = logits + (live ? t : 0) * E;
 
   uint64_t key[VPL];
+  const int e0 = j * VPL;
+  const bool vec = E == G * VPL && (VPL % 4) == 0 &&
+                   (reinterpret_cast<uintptr_t>(logits) & 15) == 0;
+  if (live && vec) {
 #pragma unroll
-  for (int i = 0; i < VPL; ++i) {
-    const int e = lane + kWave * i;
-    key[i] = e < E ? make_key(__builtin_nontemporal_load(row + e), e) : 0ull;
+    for (int v = 0; v < VPL; v += 4) {
+      const f32x4 q = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(row + e0 + v));
+#pragma unroll
+      for (int u = 0; u < 4; ++u) key[v + u] = make_key(q[u], e0 + v + u);
+    }
+  } else {
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) {
+      const int e = e0 + v;
+      key[v] = (live && e < E) ? make_key(__builtin_nontemporal_load(row + e), e) : 0ull;
+    }
   }
 
   int my_e = 0;
   float my_l = 0.f, l_max = 0.f;
-  for (int j = 0; j < k; ++j) {
+  for (int r = 0; r < k; ++r) {
     uint64_t best = key[0];
 #pragma unroll
-    for (int i = 1; i < VPL; ++i) best = key[i] > best ? key[i] : best;
-    best = wave_max_u64(best);
+    for (int v = 1; v < VPL; ++v) best = key[v] > best ? key[v] : best;
+    best = group_max_u64<G>(best);
 #pragma unroll
-    for (int i = 0; i < VPL; ++i) key[i] = key[i] == best ? 0ull : key[i];
-    const int e = static_cast<int>(~static_cast<uint32_t>(best));
+    for (int v = 0; v < VPL; ++v) key[v] = key[v] == best ? 0ull : key[v];
     const float l = from_ordered(static_cast<uint32_t>(best >> 32));
-    if (j == 0) l_max = l;
-    if (lane == j) {
-      my_e = e;
+    if (r == 0) l_max = l;
+    if (j == r) {
+      my_e = static_cast<int>(~static_cast<uint32_t>(best));
       my_l = l;
     }
   }
 
   // softmax over the selected logits, fp32
-  float ex = lane < k ? expf(my_l - l_max) : 0.f;
+  const float ex = j < k ? expf(my_l - l_max) : 0.f;
   float sum = ex;
 #pragma unroll
-  for (int off = 1; off < 16; off <<= 1) sum += __shfl_xor(sum, off, kWave);
-  // lanes 0..15 now all hold the sum over lanes 0..15 (k <= 16)
-  if (lane < k) {
-    idx_out[t * k + lane] = my_e;
-    w_out[t * k + lane] = ex / sum;
+  for (int off = G / 2; off >= 1; off >>= 1) sum += __shfl_xor(sum, off, kWave);
+  if (live && j < k) {
+    idx_out[t * k + j] = my_e;
+    w_out[t * k + j] = ex / sum;
   }
+}
+
+template <int G, int VPL>
+void launch(const float* logits, int64_t T, int E, int k, int32_t* idx, float* w, hipStream_t s) {
+  const int64_t per_block = 256 / G;
+  const dim3 grid(static_cast<unsigned>((T + per_block - 1) / per_block));
+  route_kernel<G, VPL><<<grid, 256, 0, s>>>(logits, T, E, k, idx, w);
 }
 
 }  // namespace
@@ -97,17 +121,22 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
 hipError_t launch_route(const float* logits, int64_t T, int E, int k, int32_t* idx, float* w,
                         hipStream_t s) {
   if (T == 0) return hipSuccess;
-  const dim3 block(256), grid(static_cast<unsigned>((T + 3) / 4));
-  if (E <= 64)
-    route_kernel<1><<<grid, block, 0, s>>>(logits, T, E, k, idx, w);
+  if (E <= 8)
+    launch<8, 1>(logits, T, E, k, idx, w, s);
+  else if (E <= 16 && k <= 8)
+    launch<8, 2>(logits, T, E, k, idx, w, s);
+  else if (E <= 32 && k <= 8)
+    launch<8, 4>(logits, T, E, k, idx, w, s);
+  else if (E <= 64 && k <= 8)
+    launch<8, 8>(logits, T, E, k, idx, w, s);
+  else if (E <= 64)
+    launch<16, 4>(logits, T, E, k, idx, w, s);
   else if (E <= 128)
-    route_kernel<2><<<grid, block, 0, s>>>(logits, T, E, k, idx, w);
+    launch<16, 8>(logits, T, E, k, idx, w, s);
   else if (E <= 256)
-    route_kernel<4><<<grid, block, 0, s>>>(logits, T, E, k, idx, w);
-  else if (E <= 512)
-    route_kernel<8><<<grid, block, 0, s>>>(logits, T, E, k, idx, w);
+    launch<16, 16>(logits, T, E, k, idx, w, s);
   else
-    route_kernel<16><<<grid, block, 0, s>>>(logits, T, E, k, idx, w);
+    launch<32, 32>(logits, T, E, k, idx, w, s);
   return hipGetLastError();
 }
 

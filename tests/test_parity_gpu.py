@@ -39,6 +39,14 @@ EXTRA = {
                           inter=128, ep_size=1, local_rank=-1, align=16),
     "wide": MoEConfig(name="wide", num_tokens=256, hidden=128, num_experts=1024, top_k=16,
                       inter=128, ep_size=1, local_rank=-1, align=128, dists=("zipf",)),
+    # just under the single-workgroup layout limit (4096 assignments), ragged
+    "fused_edge": MoEConfig(name="fused_edge", num_tokens=1020, hidden=128, num_experts=32,
+                            top_k=4, inter=128, ep_size=4, local_rank=3, align=32,
+                            dists=("severe",), shares=(3,)),
+    # 160000 assignments: several layout tiles per source rank
+    "tiled": MoEConfig(name="tiled", num_tokens=40000, hidden=128, num_experts=64, top_k=4,
+                       inter=128, ep_size=2, local_rank=1, align=64, dists=("mild",),
+                       shares=(1,)),
 }
 
 
@@ -46,11 +54,12 @@ def cfg_of(name):
     return EXTRA[name] if name in EXTRA else workloads.get(name)
 
 
-FULL = {"tiny", "ragged", "top1_odd", "wide"}  # oracle runs these whole
+FULL = {"tiny", "ragged", "top1_odd", "wide", "tiled", "fused_edge"}  # oracle runs these whole
 
 CASES = [("tiny", "balanced", s) for s in (-1, 0, 1)]
 CASES += [("ragged", "mild", -1), ("ragged", "mild", 2), ("top1_odd", "balanced", -1),
-          ("wide", "zipf", -1)]
+          ("wide", "zipf", -1), ("tiled", "mild", 1), ("tiled", "mild", -1),
+          ("fused_edge", "severe", 3), ("fused_edge", "severe", -1)]
 CASES += [("mixtral_8x7b", "balanced", -1), ("qwen3_30b_a3b", "zipf", -1)]
 CASES += [("deepseek_v3_ep8_share", d, 0) for d in ("balanced", "mild", "severe")]
 CASES += [("deepseek_v3_large", "severe", -1)]

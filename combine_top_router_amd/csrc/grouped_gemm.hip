@@ -19,10 +19,15 @@
 //    consecutive K values of one row of A and one row of B^T, so both
 //    operands are read K-contiguous (weights are stored output-major,
 //    [E, N, K], by the one-time repack).
-//  * 8 wavefronts per workgroup (2 per SIMD), each owning a 64-row block of
-//    accumulators. Workgroup tile: BM rows x BN staged B rows; the gated pair
-//    stages 128 gate + 128 up rows for 128 output columns, so one epilogue
-//    sees both halves of each SwiGLU product.
+//  * 8 wavefronts per workgroup (2 per SIMD), each owning TM 32-row blocks
+//    of accumulators. The main tile is 320 rows x 256 staged B rows, waves 2
+//    (rows) x 4 (columns), 160 rows x 64 B rows each: 160 accumulator VGPRs,
+//    the most two wavefronts per SIMD can hold beside their fragments. 320
+//    rows rather than 256 because expert groups a little over 256 rows (the
+//    usual case at 256 tokens per expert) then stay one tile instead of two
+//    tiles of half height. The gated pair stages 128 gate + 128 up rows for
+//    128 output columns, so one epilogue sees both halves of each SwiGLU
+//    product.
 //  * Operands go memory -> LDS with buffer_load ... lds (16 bytes per lane,
 //    no register staging) through a ring of STAGES K-slices: slice kt+STAGES-1
 //    is in flight while the matrix cores consume slice kt, one barrier per
@@ -40,7 +45,8 @@
 //  * Each tile's A range ends at its expert's last row: the rows past it
 //    read as zeros through the buffer bound (their results are never stored).
 //  * Epilogue through LDS: fp32 -> bf16 (SwiGLU for the gated pair) into a
-//    [BM, OUT_N] tile, then 16-byte row-contiguous stores of the valid rows.
+//    [BM, OUT_N] tile, then 16-byte row-contiguous stores of the valid rows;
+//    a tile larger than the stage buffers goes out in two column passes.
 #include <algorithm>
 #include <type_traits>
 
@@ -116,10 +122,10 @@ __device__ __forceinline__ int swz(int row, int ch) {
   return row * (BK * 2) + ((ch ^ swz_key<BK>(row)) << 4);
 }
 
-template <int BM, int BN, int BK, int STAGES, bool GATED>
+template <int BM, int BN, int BK, int STAGES, bool GATED, int TM>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
-  constexpr int WAVES_M = BM / 64, WAVES_N = kWaves / WAVES_M;
-  constexpr int TM = 2;
+  constexpr int WROWS = 32 * TM;               // accumulator rows per wavefront
+  constexpr int WAVES_M = BM / WROWS, WAVES_N = kWaves / WAVES_M;
   constexpr int OUT_N = GATED ? BN / 2 : BN;  // output columns per tile
   constexpr int WCOL = OUT_N / WAVES_N;       // output columns per wavefront
   constexpr int TN = (GATED ? 2 : 1) * WCOL / 32;
@@ -129,8 +135,13 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
   constexpr int CPR = BK / 8;           // 16-byte chunks per staged row
   constexpr int RB = 64 / CPR;          // rows per 1 KiB wave-load
   constexpr int WAIT = (STAGES - 2) * (A_LOADS + B_LOADS);
+  static_assert(WAVES_M * WROWS == BM && WAVES_M * WAVES_N == kWaves, "wavefront grid");
+  static_assert(A_LOADS * 1024 * kWaves == A_BYTES && B_LOADS * 1024 * kWaves == B_BYTES,
+                "whole 1 KiB wave-loads");
   static_assert(A_LOADS >= 1 && B_LOADS >= 1 && WCOL % 32 == 0 && HALF >= 1, "tile shape");
-  static_assert(STAGE * STAGES >= BM * OUT_N * 2, "epilogue tile must fit the stages");
+  // the bf16 output tile goes out through the stage buffers in EP column passes
+  constexpr int EP = (BM * OUT_N * 2 > STAGE * STAGES) ? 2 : 1;
+  static_assert(BM * OUT_N * 2 <= EP * STAGE * STAGES && WAVES_N % EP == 0, "epilogue passes");
   static_assert(!GATED || (B_LOADS % 2 == 0), "gated B loads split evenly");
 
   __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE];
@@ -142,12 +153,13 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
   const int K = g.k, N = g.n;
   const int NT = N / OUT_N, KT = K / BK;
 
-  // m-tiles per local expert, exclusive prefix (each thread: 2 experts)
+  // m-tiles per local expert, exclusive prefix (each thread: PER experts)
+  constexpr int PER = kMaxExperts / kThreads;
   {
-    int v[2], run = 0;
+    int v[PER], run = 0;
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int e = tid * 2 + q;
+    for (int q = 0; q < PER; ++q) {
+      const int e = tid * PER + q;
       v[q] = e < g.e_loc ? (g.counts[e] + BM - 1) / BM : 0;
       run += v[q];
     }
@@ -163,8 +175,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
     for (int w = 0; w < wid; ++w) before += wave_tot[w];
     int ex = before + incl - run;
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int e = tid * 2 + q;
+    for (int q = 0; q < PER; ++q) {
+      const int e = tid * PER + q;
       if (e < g.e_loc) mt_prefix[e] = ex;
       ex += v[q];
     }
@@ -246,7 +258,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
 
     // 32-row blocks of this wavefront that hold valid rows (0..TM): a partly
     // filled tile skips the matrix work (and A reads) of its empty blocks
-    const int nblk = uniform(min(TM, max(0, (rows_valid - wm * 64 + 31) / 32)));
+    const int nblk = uniform(min(TM, max(0, (rows_valid - wm * WROWS + 31) / 32)));
 
     constexpr int KK = BK / 16;
     // The K loop for NB (compile-time) valid 32-row blocks, software-pipelined
@@ -262,7 +274,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
 #pragma unroll
         for (int i = 0; i < NB; ++i)
           a[i] = *reinterpret_cast<const bf16x8*>(
-              base + swz<BK>(wm * 64 + i * 32 + (lane & 31), ch));
+              base + swz<BK>(wm * WROWS + i * 32 + (lane & 31), ch));
         if (NB == 0) return;
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
@@ -304,43 +316,54 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
         mfma(fa[(KK - 1) & 1], fb[(KK - 1) & 1]);
       }
     };
-    switch (nblk) {
-      case TM: kloop(std::integral_constant<int, TM>{}); break;
-      case 1: kloop(std::integral_constant<int, 1>{}); break;
-      default: kloop(std::integral_constant<int, 0>{}); break;
-    }
+    // one K-loop copy per supported block count; a count without its own copy
+    // runs the next larger one (the extra blocks multiply rows that are never
+    // stored)
+    if (nblk > TM / 2 + 1 || nblk == TM) kloop(std::integral_constant<int, TM>{});
+    else if (TM > 2 && nblk > 1) kloop(std::integral_constant<int, TM / 2 + 1>{});
+    else if (nblk == 1) kloop(std::integral_constant<int, 1>{});
+    else kloop(std::integral_constant<int, 0>{});
     __syncthreads();  // every wavefront is done reading the last slice
 
     // accumulators (lane: column lane % 32, rows 8*(q/4) + 4*(lane/32) + q%4)
-    // -> bf16 tile in LDS -> 16-byte stores of the valid rows
+    // -> bf16 tile in LDS -> 16-byte stores of the valid rows. A tile larger
+    // than the stage buffers goes out in EP passes, each over the columns of
+    // WAVES_N / EP wavefront columns.
+    constexpr int PN = OUT_N / EP;  // output columns per pass
+    constexpr int OCH = PN / 8;     // 16-byte chunks per output row of a pass
     uint16_t* ct = reinterpret_cast<uint16_t*>(smem);
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+    for (int pass = 0; pass < EP; ++pass) {
+      if (wn / (WAVES_N / EP) == pass) {
 #pragma unroll
-      for (int j = 0; j < HALF; ++j)
+        for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int q = 0; q < 16; ++q) {
-          const int r = wm * 64 + i * 32 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
-          const int col = wn * WCOL + j * 32 + (lane & 31);
-          float v = acc[i][j][q];
-          if constexpr (GATED) v = silu(v) * acc[i][j + HALF][q];
-          ct[r * OUT_N + col] = to_bf16(v);
-        }
-    __syncthreads();
-    constexpr int OCH = OUT_N / 8;  // 16-byte chunks per output row
-    uint16_t* C = g.c + row0 * N + int64_t(nt) * OUT_N;
-    for (int c = tid; c < rows_valid * OCH; c += kThreads) {
-      const int r = c / OCH, ch = c % OCH;
-      *reinterpret_cast<u32x4*>(C + int64_t(r) * N + ch * 8) =
-          *reinterpret_cast<const u32x4*>(ct + r * OUT_N + ch * 8);
+          for (int j = 0; j < HALF; ++j)
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+              const int r = wm * WROWS + i * 32 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
+              const int col = wn * WCOL + j * 32 + (lane & 31) - pass * PN;
+              float v = acc[i][j][q];
+              if constexpr (GATED) v = silu(v) * acc[i][j + HALF][q];
+              ct[r * PN + col] = to_bf16(v);
+            }
+      }
+      __syncthreads();
+      uint16_t* C = g.c + row0 * N + int64_t(nt) * OUT_N + pass * PN;
+      for (int c = tid; c < rows_valid * OCH; c += kThreads) {
+        const int r = c / OCH, ch = c % OCH;
+        *reinterpret_cast<u32x4*>(C + int64_t(r) * N + ch * 8) =
+            *reinterpret_cast<const u32x4*>(ct + r * PN + ch * 8);
+      }
+      if (pass + 1 < EP) __syncthreads();  // pass read out before the next one is written
     }
     __syncthreads();  // the tile buffer is read out before the next tile's loads
   }
 }
 
-template <int BM, int BN, int BK, int STAGES, bool GATED>
+template <int BM, int BN, int BK, int STAGES, bool GATED, int TM>
 hipError_t launch(const GemmArgs& a, hipStream_t s) {
-  grouped_gemm_kernel<BM, BN, BK, STAGES, GATED><<<device_cu_count(), kThreads, 0, s>>>(a);
+  grouped_gemm_kernel<BM, BN, BK, STAGES, GATED, TM><<<device_cu_count(), kThreads, 0, s>>>(a);
   return hipGetLastError();
 }
 
@@ -353,7 +376,7 @@ hipError_t launch_gate_up(const void* x_perm, const int32_t* offsets, const int3
   const GemmArgs a{static_cast<const uint16_t*>(x_perm), static_cast<const uint16_t*>(w1t),
                    static_cast<const uint16_t*>(w3t), static_cast<uint16_t*>(h), offsets, counts,
                    e_loc, I, H};
-  return launch<256, 256, 64, 2, true>(a, s);  // I % 128 == 0: 128 output columns per tile
+  return launch<320, 256, 64, 2, true, 5>(a, s);  // I % 128 == 0: 128 output columns per tile
 }
 
 hipError_t launch_down(const void* h, const int32_t* offsets, const int32_t* counts, int e_loc,
@@ -361,8 +384,8 @@ hipError_t launch_down(const void* h, const int32_t* offsets, const int32_t* cou
   (void)m_cap;
   const GemmArgs a{static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(w2t), nullptr,
                    static_cast<uint16_t*>(y), offsets, counts, e_loc, H, I};
-  if (H % 256 == 0) return launch<256, 256, 64, 2, false>(a, s);
-  return launch<256, 128, 64, 2, false>(a, s);
+  if (H % 256 == 0) return launch<320, 256, 64, 2, false, 5>(a, s);
+  return launch<256, 128, 64, 2, false, 2>(a, s);
 }
 
 }  // namespace moe

@@ -7,8 +7,9 @@ method does floating point) of what the HIP library computes:
   layout   -> ``oracle.layout``    histogram, split plan, padded offsets, stable permutation
   permute  -> ``oracle.permute``   expert-major row gather
   experts  -> ``oracle.experts``   per-expert SwiGLU MLP
-  combine  -> ``oracle.combine``   weighted un-permute with fp64 sums, one bf16 rounding
+  combine  -> ``oracle.combine``   weighted un-permute, fp32 slot-order sums, one bf16 rounding
   layer    -> ``oracle.layer``     the composition, and per-token outputs for sampling
+  backward -> ``oracle.backward``  gradients of route, permute and combine
 
 It shares no code with the HIP path and imports nothing from it. Only the
 tests, the smoke check and the benchmark's CPU-baseline leg may import it;
@@ -19,4 +20,4 @@ Pinned by ``tests/test_oracle_*.py`` against a hand-computed worked example
 invariants the pages state. Parity unpinned: nothing (every function has at
 least one pin that does not re-run its own formula).
 """
-from . import bf16, checks, combine, experts, layer, layout, permute, route  # noqa: F401
+from . import backward, bf16, checks, combine, experts, layer, layout, permute, route  # noqa: F401

@@ -46,6 +46,9 @@ SIGNATURES = {
     "moe_grouped_down": (_I32, [_P, _P, _P, _I32, _I64, _I32, _I32, _P, _P, _P]),
     "moe_grouped_swiglu": (_I32, [_P, _P, _P, _I32, _I64, _I32, _I32, _P, _P, _P, _P, _P, _P]),
     "moe_combine": (_I32, [_P, _I64, _P, _P, _I64, _I32, _I32, _P, _P]),
+    "moe_combine_backward": (_I32, [_P, _P, _I64, _P, _P, _I64, _I32, _I32, _P, _P, _P]),
+    "moe_permute_backward": (_I32, [_P, _I64, _P, _I64, _I32, _I32, _P, _P]),
+    "moe_route_backward": (_I32, [_P, _P, _P, _I64, _I32, _I32, _P, _P]),
     "moe_validate_layout": (_I32, [C.POINTER(LayoutDesc), _P, _P, _P, _P, _I64, _P, C.c_char_p,
                                    _SZ]),
 }

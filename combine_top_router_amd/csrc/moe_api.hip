@@ -202,6 +202,50 @@ int32_t moe_combine(const void* y_d, int64_t y_rows, const int32_t* dst_row_d,
                                        top_k, out_d, as_stream(stream)));
 }
 
+int32_t moe_combine_backward(const void* grad_out_d, const void* y_d, int64_t y_rows,
+                             const int32_t* dst_row_d, const float* topk_w_d, int64_t num_tokens,
+                             int32_t hidden, int32_t top_k, void* grad_y_d, float* grad_w_d,
+                             void* stream) {
+  if (num_tokens < 0 || y_rows < 0 || hidden < 8 || hidden > kMaxHidden || hidden % 8 ||
+      top_k < 1 || top_k > kMaxTopK)
+    return MOE_ERR_ARG;
+  if (num_tokens == 0) return MOE_OK;
+  if (!grad_out_d || !dst_row_d || !topk_w_d || !grad_w_d || !aligned16(grad_out_d))
+    return MOE_ERR_ARG;
+  if (y_rows > 0 && (!y_d || !grad_y_d || !aligned16(y_d) || !aligned16(grad_y_d)))
+    return MOE_ERR_ARG;
+  return status_of(moe::launch_combine_backward(grad_out_d, y_d, y_rows, dst_row_d, topk_w_d,
+                                                num_tokens, hidden, top_k, grad_y_d, grad_w_d,
+                                                as_stream(stream)));
+}
+
+int32_t moe_permute_backward(const void* grad_x_perm_d, int64_t x_perm_rows,
+                             const int32_t* dst_row_d, int64_t num_tokens, int32_t hidden,
+                             int32_t top_k, void* grad_x_d, void* stream) {
+  if (num_tokens < 0 || x_perm_rows < 0 || hidden < 8 || hidden > kMaxHidden || hidden % 8 ||
+      top_k < 1 || top_k > kMaxTopK)
+    return MOE_ERR_ARG;
+  if (num_tokens == 0) return MOE_OK;
+  if (!dst_row_d || !grad_x_d || !aligned16(grad_x_d)) return MOE_ERR_ARG;
+  if (x_perm_rows > 0 && (!grad_x_perm_d || !aligned16(grad_x_perm_d))) return MOE_ERR_ARG;
+  return status_of(moe::launch_combine(grad_x_perm_d, x_perm_rows, dst_row_d, nullptr,
+                                       num_tokens, hidden, top_k, grad_x_d, as_stream(stream)));
+}
+
+int32_t moe_route_backward(const int32_t* topk_idx_d, const float* topk_w_d,
+                           const float* grad_w_d, int64_t num_tokens, int32_t num_experts,
+                           int32_t top_k, float* grad_logits_d, void* stream) {
+  if (num_tokens < 0 || num_experts < 1 || num_experts > kMaxExperts || top_k < 1 ||
+      top_k > std::min(num_experts, kMaxTopK))
+    return MOE_ERR_ARG;
+  if (num_tokens > int64_t(UINT32_MAX) / num_experts) return MOE_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return MOE_OK;
+  if (!topk_idx_d || !topk_w_d || !grad_w_d || !grad_logits_d) return MOE_ERR_ARG;
+  return status_of(moe::launch_route_backward(topk_idx_d, topk_w_d, grad_w_d, num_tokens,
+                                              num_experts, top_k, grad_logits_d,
+                                              as_stream(stream)));
+}
+
 int32_t moe_validate_layout(const moe_layout_desc* desc, const int32_t* topk_idx_d,
                             const int32_t* offsets_d, const int32_t* dst_row_d,
                             const int32_t* src_row_d, int64_t m_cap, void* stream, char* detail,

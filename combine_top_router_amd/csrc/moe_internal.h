@@ -86,6 +86,12 @@ hipError_t launch_permute(const void* x, int64_t T, int H, int k, const int32_t*
                           int64_t m_cap, void* x_perm, hipStream_t s);
 hipError_t launch_combine(const void* y, int64_t y_rows, const int32_t* dst_row, const float* w,
                           int64_t T, int H, int k, void* out, hipStream_t s);
+hipError_t launch_combine_backward(const void* grad_out, const void* y, int64_t y_rows,
+                                   const int32_t* dst_row, const float* w, int64_t T, int H,
+                                   int k, void* grad_y, float* grad_w, hipStream_t s);
+hipError_t launch_route_backward(const int32_t* topk_idx, const float* topk_w,
+                                 const float* grad_w, int64_t T, int E, int k,
+                                 float* grad_logits, hipStream_t s);
 hipError_t launch_pack(const void* w, int64_t mats, int rows, int cols, void* wt, hipStream_t s);
 
 hipError_t launch_gate_up(const void* x_perm, const int32_t* offsets, const int32_t* counts,

@@ -13,6 +13,8 @@
 //   "Problem", "Change", "Benchmark"): per token, sum over slots in slot order
 //   of fp32 weight x bf16 row, products and sums in fp32, one rounding to
 //   bf16; rows addressed through dst_row (flat index token*top_k + slot).
+//   Without a weight array every weight is 1: the sum of a token's local row
+//   gradients, which is the permute's backward (a combine, DeepEP issue #272).
 #include "moe_internal.h"
 
 namespace moe {
@@ -92,7 +94,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const u32x4* __restrict__ 
     if (j < k) {
       const int r = dst_row[t * k + j];
       rows[j] = (r >= 0 && r < y_rows) ? int64_t(r) : -1;
-      w[j] = topk_w[t * k + j];
+      w[j] = topk_w ? topk_w[t * k + j] : 1.0f;  // no weights: the permute's backward
     } else {
       rows[j] = -1;
       w[j] = 0.f;

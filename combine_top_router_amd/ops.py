@@ -229,3 +229,59 @@ def combine(y: torch.Tensor, dst_row: torch.Tensor, topk_w: torch.Tensor, out=No
     check("moe_combine", lib().moe_combine(_ptr(y), y.shape[0], _ptr(dst_row), _ptr(topk_w), T,
                                            H, k, _ptr(out), _stream(y.device)))
     return out
+
+
+# ---------------------------------------------------------------- backward
+
+def combine_backward(grad_out: torch.Tensor, y: torch.Tensor, dst_row: torch.Tensor,
+                     topk_w: torch.Tensor, grad_y=None, grad_w=None):
+    """(grad_y [y_rows, H] bf16, grad_w [T, k] fp32): the row gradient
+    bf16(w * G) written to each local row, the score gradient <G[t], y[r]>
+    (0 for slots on other shares). Rows no slot points at are left as given."""
+    _need(grad_out, "grad_out", torch.bfloat16)
+    _need(y, "y", torch.bfloat16)
+    _need(dst_row, "dst_row", torch.int32)
+    T, k = dst_row.shape
+    H = grad_out.shape[1]
+    _need(topk_w, "topk_w", torch.float32, (T, k))
+    _need(grad_out, "grad_out", torch.bfloat16, (T, H))
+    _need(y, "y", torch.bfloat16, (y.shape[0], H))
+    grad_y = _empty(tuple(y.shape), torch.bfloat16, y.device) if grad_y is None else grad_y
+    grad_w = _empty((T, k), torch.float32, y.device) if grad_w is None else grad_w
+    _need(grad_y, "grad_y", torch.bfloat16, tuple(y.shape))
+    _need(grad_w, "grad_w", torch.float32, (T, k))
+    check("moe_combine_backward", lib().moe_combine_backward(
+        _ptr(grad_out), _ptr(y), y.shape[0], _ptr(dst_row), _ptr(topk_w), T, H, k,
+        _ptr(grad_y), _ptr(grad_w), _stream(y.device)))
+    return grad_y, grad_w
+
+
+def permute_backward(grad_x_perm: torch.Tensor, dst_row: torch.Tensor, out=None):
+    """grad_x [T, H] bf16: per token, the fp32 slot-order sum of its local row
+    gradients, rounded once (zero row without a local slot)."""
+    _need(grad_x_perm, "grad_x_perm", torch.bfloat16)
+    _need(dst_row, "dst_row", torch.int32)
+    T, k = dst_row.shape
+    H = grad_x_perm.shape[1]
+    out = _empty((T, H), torch.bfloat16, grad_x_perm.device) if out is None else out
+    _need(out, "grad_x", torch.bfloat16, (T, H))
+    check("moe_permute_backward", lib().moe_permute_backward(
+        _ptr(grad_x_perm), grad_x_perm.shape[0], _ptr(dst_row), T, H, k, _ptr(out),
+        _stream(out.device)))
+    return out
+
+
+def route_backward(topk_idx: torch.Tensor, topk_w: torch.Tensor, grad_w: torch.Tensor,
+                   num_experts: int, out=None):
+    """grad_logits [T, E] fp32: w_j (g_j - sum_i w_i g_i) at the selected
+    experts, zero elsewhere."""
+    _need(topk_idx, "topk_idx", torch.int32)
+    T, k = topk_idx.shape
+    _need(topk_w, "topk_w", torch.float32, (T, k))
+    _need(grad_w, "grad_w", torch.float32, (T, k))
+    out = _empty((T, num_experts), torch.float32, topk_idx.device) if out is None else out
+    _need(out, "grad_logits", torch.float32, (T, num_experts))
+    check("moe_route_backward", lib().moe_route_backward(
+        _ptr(topk_idx), _ptr(topk_w), _ptr(grad_w), T, num_experts, k, _ptr(out),
+        _stream(out.device)))
+    return out

@@ -218,8 +218,8 @@ int32_t moe_grouped_swiglu(const void* x_perm_d, const int32_t* offsets_d,
  *   out[t, :] = bf16( sum over slots s = 0..k-1 with 0 <= dst_row[t, s] < y_rows
  *                     of topk_w[t, s] * y[dst_row[t, s], :] )
  *
- * summed in fp32 in slot order (fused multiply-add), rounded once to bf16
- * (nearest even). A token with no local slot gets a zero row. The result
+ * summed in fp32 in slot order (each product rounded to fp32, then added:
+ * no fused multiply-add), rounded once to bf16 (nearest even). A token with no local slot gets a zero row. The result
  * does not depend on where the rows sit in y.
  *   y_d       [y_rows, H] bf16, 16-byte aligned
  *   dst_row_d [T, k] int32;  topk_w_d [T, k] float
@@ -229,6 +229,54 @@ int32_t moe_grouped_swiglu(const void* x_perm_d, const int32_t* offsets_d,
 int32_t moe_combine(const void* y_d, int64_t y_rows, const int32_t* dst_row_d,
                     const float* topk_w_d, int64_t num_tokens, int32_t hidden,
                     int32_t top_k, void* out_d, void* stream);
+
+/*
+ * Backward of the combine, the permute and the routing weights.
+ *
+ * The fused restore back-propagates a row gradient and a score gradient, the
+ * score (router) gradient in FP32 (DeepSpeed PR #8847, sections "Tests" and
+ * "Benchmark"); the backward of a combine is a dispatch of the output
+ * gradient and the backward of a dispatch is a combine (DeepEP issue #272,
+ * the maintainer's answer). G is the gradient of the combine's output.
+ *
+ * moe_combine_backward: for every (t, s) with 0 <= r = dst_row[t, s] < y_rows
+ *   grad_y[r, :]  = bf16(topk_w[t, s] * G[t, :])    (fp32 product, one rounding)
+ *   grad_w[t, s]  = sum_h G[t, h] * y[r, h]          (fp32, tree-shaped sum)
+ * and grad_w[t, s] = 0 for every other slot. Rows of grad_y that no slot
+ * points at are not written.
+ *   grad_out_d [T, H] bf16;  y_d [y_rows, H] bf16 (the forward's expert output)
+ *   dst_row_d, topk_w_d [T, k] as in moe_combine
+ *   grad_y_d   [y_rows, H] bf16 (out);  grad_w_d [T, k] float (out)
+ * Limits as moe_combine; bf16 pointers 16-byte aligned.
+ */
+int32_t moe_combine_backward(const void* grad_out_d, const void* y_d, int64_t y_rows,
+                             const int32_t* dst_row_d, const float* topk_w_d,
+                             int64_t num_tokens, int32_t hidden, int32_t top_k,
+                             void* grad_y_d, float* grad_w_d, void* stream);
+
+/*
+ * moe_permute_backward: grad_x[t, :] = bf16( sum over slots s with
+ *   0 <= dst_row[t, s] < x_perm_rows of grad_x_perm[dst_row[t, s], :] ),
+ * an fp32 sum in slot order rounded once (moe_combine with unit weights); a
+ * token with no local slot gets a zero row.
+ *   grad_x_perm_d [x_perm_rows, H] bf16;  grad_x_d [T, H] bf16 (out)
+ * Limits as moe_combine.
+ */
+int32_t moe_permute_backward(const void* grad_x_perm_d, int64_t x_perm_rows,
+                             const int32_t* dst_row_d, int64_t num_tokens, int32_t hidden,
+                             int32_t top_k, void* grad_x_d, void* stream);
+
+/*
+ * moe_route_backward: the routing weights are the softmax of the k selected
+ * logits (moe_route), so with g = grad_w[t, :] (the score gradient)
+ *   grad_logits[t, topk_idx[t, j]] = topk_w[t, j] * (g_j - sum_i topk_w[t, i] * g_i)
+ * (the sum in fp32, slot order) and 0 for every unselected expert.
+ *   topk_idx_d, topk_w_d, grad_w_d [T, k];  grad_logits_d [T, E] float (out)
+ * Limits as moe_route; T * E < 2^32 (else MOE_ERR_UNSUPPORTED).
+ */
+int32_t moe_route_backward(const int32_t* topk_idx_d, const float* topk_w_d,
+                           const float* grad_w_d, int64_t num_tokens, int32_t num_experts,
+                           int32_t top_k, float* grad_logits_d, void* stream);
 
 /*
  * moe_validate_layout -- debug check of a layout (SYNCHRONISES the stream,

@@ -113,3 +113,15 @@ def expert_outputs(cfg: MoEConfig, rows: int, seed: int = 0, device="cpu") -> to
     """Stand-in expert outputs ``y`` [rows, H] bf16, N(0, 1), for exercising the
     combine on its own."""
     return _randn((rows, cfg.hidden), 1.0, device, cfg.name, "y", seed).to(torch.bfloat16)
+
+
+def output_gradient(cfg: MoEConfig, seed: int = 0, device="cpu") -> torch.Tensor:
+    """Stand-in gradient of the layer output ``G`` [T, H] bf16, N(0, 1), for
+    the backward steps."""
+    return _randn((cfg.num_tokens, cfg.hidden), 1.0, device, cfg.name, "grad_out",
+                  seed).to(torch.bfloat16)
+
+
+def score_gradient(cfg: MoEConfig, seed: int = 0, device="cpu") -> torch.Tensor:
+    """Stand-in gradient of the routing weights [T, k] fp32, N(0, 1)."""
+    return _randn((cfg.num_tokens, cfg.top_k), 1.0, device, cfg.name, "grad_w", seed)

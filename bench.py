@@ -44,6 +44,8 @@ def parse():
     ap.add_argument("--dist", default=None)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip timing the backward calls (combine, permute, routing)")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for the CPU baseline sample")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -141,6 +143,53 @@ def cpu_baseline(cfg, dist, layer_args, budget_s):
                        f"layer (route, layout, permute, fp64 SwiGLU experts, fp64 combine), "
                        f"{t:.1f} s, numpy BLAS threads {threads}, "
                        f"{len(os.sched_getaffinity(0))} host cores visible")}
+
+
+def time_backward(args, cfg, layer, moe, stream, t_loc, n_loc):
+    """Per-call times of the backward calls on this step's routing and rows,
+    after the forward timing (not part of the step or of ``value``). The
+    permute gradient's input is a stand-in buffer of the x_perm shape: the
+    expert backward that would produce it is not part of this library."""
+    import numpy as np
+    import torch
+
+    import workloads
+
+    T, H, E, k = cfg.num_tokens, cfg.hidden, cfg.num_experts, cfg.top_k
+    dev = layer.y.device
+    G = workloads.gen.output_gradient(cfg, args.seed, device=dev)
+    gy = torch.zeros_like(layer.y)
+    gw = torch.empty((T, k), dtype=torch.float32, device=dev)
+    gx = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    gl = torch.empty((T, E), dtype=torch.float32, device=dev)
+    dst = layer.L.dst_row
+    calls = [
+        ("combine_backward", lambda: moe.ops.combine_backward(G, layer.y, dst, layer.topk_w, gy, gw),
+         t_loc * H * 2 + 2 * n_loc * H * 2 + T * k * 12),
+        ("permute_backward", lambda: moe.ops.permute_backward(gy, dst, gx),
+         n_loc * H * 2 + T * H * 2 + T * k * 4),
+        ("route_backward", lambda: moe.ops.route_backward(layer.topk_idx, layer.topk_w, gw, E, gl),
+         T * E * 4 + T * k * 12),
+    ]
+    reps = max(3, args.steps)
+    out = {}
+    for name, run, nbytes in calls:
+        for _ in range(3):
+            run()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        # a short device-side wait first, so the calls queue up behind it and
+        # the events time the GPU, not the host's launch rate
+        torch.cuda._sleep(4_000_000)
+        ev[0].record(stream)
+        for r in range(reps):
+            run()
+            ev[r + 1].record(stream)
+        torch.cuda.synchronize()
+        ms = float(np.mean([ev[r].elapsed_time(ev[r + 1]) for r in range(reps)]))
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        out[name] = {"ms": round(ms, 4), "bound": "hbm", "GB/s": round(gbs, 1),
+                     "frac": round(gbs / PEAK_HBM_GBS, 4), "bytes": int(nbytes)}
+    return out
 
 
 def main():
@@ -243,6 +292,9 @@ def main():
         roof = {"bound": "hbm", "kernel": dom, "achieved": d["GB/s"], "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": d["frac"], "traffic": traffic}
 
+    backward = None if args.no_backward else time_backward(args, cfg, layer, moe, stream,
+                                                            t_loc, n_loc)
+
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
@@ -257,7 +309,7 @@ def main():
                    "local_experts": len(cfg.local_experts(share)), "top_k": k, "inter": I,
                    "ep_size": cfg.ep_size, "local_rank": share, "align": cfg.align,
                    "routing": dist, "local_rows": n_loc, "seed": args.seed},
-        "roofline": roof, "stages": stage_out, "cpu_baseline": cpu,
+        "roofline": roof, "stages": stage_out, "backward": backward, "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
 

@@ -175,3 +175,60 @@ def test_fp32_score_gradient_error_is_the_pages_size():
     assert (np.abs(fp32 - exact) <= ob.score_bound(G, y, dst)[:, 0]).all()
     as_bf16 = bf16.round_to_bf16(exact)
     assert np.linalg.norm(as_bf16 - exact) / np.linalg.norm(exact) > 1e-4
+
+
+# ---------------------------------------------------------------- experts
+
+from oracle import experts as oexperts  # noqa: E402
+
+
+@pytest.mark.parametrize("seed", [21, 22])
+def test_expert_gradients_match_finite_differences(seed):
+    # every gradient of swiglu_backward against central differences of the
+    # forward swiglu (fp64): a swapped gate/up, a missing silu' term or a
+    # transposed weight would fail
+    rng = np.random.default_rng(seed)
+    m, H, I = 5, 6, 4
+    x = rng.standard_normal((m, H))
+    w1 = rng.standard_normal((H, I)) * 0.5
+    w3 = rng.standard_normal((H, I)) * 0.5
+    w2 = rng.standard_normal((I, H)) * 0.5
+    dy = rng.standard_normal((m, H))
+    dx, dw1, dw3, dw2 = oexperts.swiglu_backward(x, w1, w3, w2, dy)
+
+    def loss(x_, w1_, w3_, w2_):
+        return (oexperts.swiglu(x_, w1_, w3_, w2_) * dy).sum()
+
+    eps = 1e-6
+    for name, arr, grad in (("x", x, dx), ("w1", w1, dw1), ("w3", w3, dw3), ("w2", w2, dw2)):
+        for _ in range(6):
+            i = tuple(rng.integers(0, n) for n in arr.shape)
+            args = {"x": x, "w1": w1, "w3": w3, "w2": w2}
+            plus = {k: v.copy() for k, v in args.items()}
+            minus = {k: v.copy() for k, v in args.items()}
+            plus[name][i] += eps
+            minus[name][i] -= eps
+            fd = (loss(plus["x"], plus["w1"], plus["w3"], plus["w2"]) -
+                  loss(minus["x"], minus["w1"], minus["w3"], minus["w2"])) / (2 * eps)
+            assert fd == pytest.approx(grad[i], rel=1e-6, abs=1e-8), (name, i)
+
+
+def test_expert_data_gradient_closed_form():
+    # H = I = 1: y = silu(a x) (b x) c, so dy/dx = c (a b x) (2 s + a x s (1 - s))
+    # with s = sigmoid(a x): checks silu' and the product rule by hand
+    a, b, c, x = 0.7, -1.3, 2.0, 0.9
+    dx = oexperts.swiglu_backward([[x]], [[a]], [[b]], [[c]], [[1.0]])[0][0, 0]
+    s = 1.0 / (1.0 + np.exp(-a * x))
+    assert dx == pytest.approx(c * a * b * x * (2 * s + a * x * s * (1 - s)), rel=1e-12)
+
+
+def test_grouped_data_gradient_leaves_padding_zero():
+    rng = np.random.default_rng(3)
+    H, I = 4, 3
+    ws = [tuple(rng.standard_normal(s) for s in ((H, I), (H, I), (I, H))) for _ in range(2)]
+    offsets, counts = [0, 4, 8], [3, 2]
+    xp = rng.standard_normal((8, H))
+    dy = rng.standard_normal((8, H))
+    dx = oexperts.grouped_swiglu_backward_data(xp, dy, offsets, counts, lambda e: ws[e])
+    assert not dx[3].any() and not dx[6:].any()
+    np.testing.assert_allclose(dx[4:6], oexperts.swiglu_backward(xp[4:6], *ws[1], dy[4:6])[0])

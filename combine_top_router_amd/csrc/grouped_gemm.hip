@@ -59,15 +59,31 @@ constexpr int kMaxExperts = 1024;
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * kWave;
 
+// What a launch computes (the B operand is always [E_loc, N, ldb], rows
+// K-contiguous):
+//   kPlain      c = a b0^T                                  (down; any plain product)
+//   kGated      c = silu(a b0^T) * (a b1^T)                 (gate/up, SwiGLU fused)
+//   kGatedSave  as kGated, and aux_out = [a b0^T | a b1^T]  (pre-activations kept for
+//                                                            the backward), bf16
+//   kSwigluBwd  dh = a b0^T, then with (g, u) = aux:        (down backward)
+//               c = [dh u silu'(g) | dh silu(g)]
+//   kKSplit     c = a [b0 | b1]^T, b0 for k < k_split and b1 past it
+//                                                           (gate/up backward)
+enum Kind { kPlain = 0, kGated = 1, kGatedSave = 2, kSwigluBwd = 3, kKSplit = 4 };
+
 struct GemmArgs {
   const uint16_t* a;       // [rows, K] bf16
-  const uint16_t* b0;      // [E_loc, N, K] bf16
-  const uint16_t* b1;      // [E_loc, N, K] bf16 (gated only)
-  uint16_t* c;             // [rows, N] bf16
+  const uint16_t* b0;      // [E_loc, N, ldb] bf16
+  const uint16_t* b1;      // [E_loc, N, ldb] bf16 (kGated*, kKSplit)
+  uint16_t* c;             // [rows, N] bf16 ([rows, 2N] for kSwigluBwd)
   const int32_t* offsets;  // [E_loc + 1]
   const int32_t* counts;   // [E_loc]
   int e_loc;
   int n, k;
+  int ldb;                 // row length of b0/b1: K, or k_split for kKSplit
+  int k_split;             // kKSplit: K index where b1 takes over
+  const uint16_t* aux;     // kSwigluBwd: [rows, 2N] bf16, (g | u) of the forward
+  uint16_t* aux_out;       // kGatedSave: [rows, 2N] bf16 (out)
 };
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
@@ -122,8 +138,9 @@ __device__ __forceinline__ int swz(int row, int ch) {
   return row * (BK * 2) + ((ch ^ swz_key<BK>(row)) << 4);
 }
 
-template <int BM, int BN, int BK, int STAGES, bool GATED, int TM>
+template <int BM, int BN, int BK, int STAGES, int KIND, int TM>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
+  constexpr bool GATED = KIND == kGated || KIND == kGatedSave;
   constexpr int WROWS = 32 * TM;               // accumulator rows per wavefront
   constexpr int WAVES_M = BM / WROWS, WAVES_N = kWaves / WAVES_M;
   constexpr int OUT_N = GATED ? BN / 2 : BN;  // output columns per tile
@@ -218,13 +235,16 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
 
     // scalar bases + 32-bit per-lane offsets (elements) within the tile
     const uint16_t* a_base = g.a + row0 * K;
-    const uint16_t* b_base0 = g.b0 + (int64_t(e) * N + int64_t(nt) * OUT_N) * K;
-    const uint16_t* b_base1 = GATED ? g.b1 + (int64_t(e) * N + int64_t(nt) * OUT_N) * K : b_base0;
+    const int ldb = g.ldb;
+    const uint16_t* b_base0 = g.b0 + (int64_t(e) * N + int64_t(nt) * OUT_N) * ldb;
+    const uint16_t* b_base1 = (GATED || KIND == kKSplit)
+                                  ? g.b1 + (int64_t(e) * N + int64_t(nt) * OUT_N) * ldb
+                                  : b_base0;
     // A's range ends at the expert's last valid row of the tile: the rows
     // past it read as zeros (their results are never stored)
     const i32x4 ra = make_rsrc(a_base, uint32_t(rows_valid) * uint32_t(K) * 2u);
-    const i32x4 rb0 = make_rsrc(b_base0, uint32_t(OUT_N) * uint32_t(K) * 2u);
-    const i32x4 rb1 = make_rsrc(b_base1, uint32_t(OUT_N) * uint32_t(K) * 2u);
+    const i32x4 rb0 = make_rsrc(b_base0, uint32_t(OUT_N) * uint32_t(ldb) * 2u);
+    const i32x4 rb1 = make_rsrc(b_base1, uint32_t(OUT_N) * uint32_t(ldb) * 2u);
     uint32_t oa[A_LOADS], ob[B_LOADS];
 #pragma unroll
     for (int i = 0; i < A_LOADS; ++i) {
@@ -234,7 +254,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
 #pragma unroll
     for (int i = 0; i < B_LOADS; ++i) {
       const int r = (wid + kWaves * i) * RB + ld_r;  // gated: first half gate rows, then up
-      ob[i] = uint32_t(GATED ? r % (BN / 2) : r) * uint32_t(K) + ld_ch * 8;
+      ob[i] = uint32_t(GATED ? r % (BN / 2) : r) * uint32_t(ldb) + ld_ch * 8;
     }
     auto issue = [&](int kt, int st) {
       const uint32_t sbase = lds0 + st * STAGE;
@@ -242,10 +262,19 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
 #pragma unroll
       for (int i = 0; i < A_LOADS; ++i)
         dma16(ra, (oa[i] + k0) * 2, sbase + (wid + kWaves * i) * 1024);
+      if constexpr (KIND == kKSplit) {
+        // the same slice of b0 or, past k_split, of b1 (slices never straddle it)
+        const bool second = k0 >= uint32_t(g.k_split);
+        const uint32_t kb = second ? k0 - uint32_t(g.k_split) : k0;
 #pragma unroll
-      for (int i = 0; i < B_LOADS; ++i)
-        dma16((GATED && i >= B_LOADS / 2) ? rb1 : rb0, (ob[i] + k0) * 2,
-              sbase + A_BYTES + (wid + kWaves * i) * 1024);
+        for (int i = 0; i < B_LOADS; ++i)
+          dma16(second ? rb1 : rb0, (ob[i] + kb) * 2, sbase + A_BYTES + (wid + kWaves * i) * 1024);
+      } else {
+#pragma unroll
+        for (int i = 0; i < B_LOADS; ++i)
+          dma16((GATED && i >= B_LOADS / 2) ? rb1 : rb0, (ob[i] + k0) * 2,
+                sbase + A_BYTES + (wid + kWaves * i) * 1024);
+      }
     };
 
     f32x16 acc[TM][TN];
@@ -326,44 +355,103 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
     __syncthreads();  // every wavefront is done reading the last slice
 
     // accumulators (lane: column lane % 32, rows 8*(q/4) + 4*(lane/32) + q%4)
-    // -> bf16 tile in LDS -> 16-byte stores of the valid rows. A tile larger
-    // than the stage buffers goes out in EP passes, each over the columns of
-    // WAVES_N / EP wavefront columns.
-    constexpr int PN = OUT_N / EP;  // output columns per pass
-    constexpr int OCH = PN / 8;     // 16-byte chunks per output row of a pass
+    // -> bf16 tile in LDS -> 16-byte stores of the valid rows. Each of the
+    // NOUT outputs goes out on its own; a tile larger than the stage buffers
+    // goes out in EP passes, each over the columns of WAVES_N / EP wavefront
+    // columns.
     uint16_t* ct = reinterpret_cast<uint16_t*>(smem);
+    if constexpr (KIND == kSwigluBwd) {
+      // one pass per wavefront column (PN = WCOL columns): the forward's g and
+      // u of the pass's columns are staged in LDS with 16-byte loads, then
+      // each output (dg, du) goes out through a third LDS tile
+      constexpr int PN = WCOL, OCH = PN / 8;
+      static_assert(3 * BM * PN * 2 <= STAGE * STAGES, "g, u and output tiles fit the stages");
+      uint16_t* gt = ct + BM * PN;
+      uint16_t* ut = gt + BM * PN;
+      for (int pass = 0; pass < WAVES_N; ++pass) {
+        const int64_t cb = int64_t(nt) * OUT_N + pass * PN;  // first column of the pass
+        for (int c = tid; c < rows_valid * OCH; c += kThreads) {
+          const int r = c / OCH, ch = c % OCH;
+          const uint16_t* src = g.aux + (row0 + r) * 2 * int64_t(N) + cb + ch * 8;
+          *reinterpret_cast<u32x4*>(gt + r * PN + ch * 8) = *reinterpret_cast<const u32x4*>(src);
+          *reinterpret_cast<u32x4*>(ut + r * PN + ch * 8) = *reinterpret_cast<const u32x4*>(src + N);
+        }
+        __syncthreads();
+        for (int o = 0; o < 2; ++o) {
+          if (wn == pass) {
 #pragma unroll
-    for (int pass = 0; pass < EP; ++pass) {
-      if (wn / (WAVES_N / EP) == pass) {
+            for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
+              for (int j = 0; j < TN; ++j)
 #pragma unroll
-          for (int j = 0; j < HALF; ++j)
-#pragma unroll
-            for (int q = 0; q < 16; ++q) {
-              const int r = wm * WROWS + i * 32 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
-              const int col = wn * WCOL + j * 32 + (lane & 31) - pass * PN;
-              float v = acc[i][j][q];
-              if constexpr (GATED) v = silu(v) * acc[i][j + HALF][q];
-              ct[r * PN + col] = to_bf16(v);
-            }
+                for (int q = 0; q < 16; ++q) {
+                  const int r = wm * WROWS + i * 32 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
+                  const int col = j * 32 + (lane & 31);  // within the pass
+                  // rows past rows_valid hold stale LDS: their results are never stored
+                  const float dh = acc[i][j][q];
+                  const float gg = from_bf16(gt[r * PN + col]);
+                  const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-gg));
+                  const float v = o == 0 ? dh * from_bf16(ut[r * PN + col]) *
+                                               (sg * (1.0f + gg * (1.0f - sg)))
+                                         : dh * (gg * sg);
+                  ct[r * PN + col] = to_bf16(v);
+                }
+          }
+          __syncthreads();
+          uint16_t* C = g.c + row0 * 2 * int64_t(N) + o * int64_t(N) + cb;
+          for (int c = tid; c < rows_valid * OCH; c += kThreads) {
+            const int r = c / OCH, ch = c % OCH;
+            *reinterpret_cast<u32x4*>(C + int64_t(r) * 2 * N + ch * 8) =
+                *reinterpret_cast<const u32x4*>(ct + r * PN + ch * 8);
+          }
+          __syncthreads();  // ct (and, after du, gt/ut) read out before the next write
+        }
       }
-      __syncthreads();
-      uint16_t* C = g.c + row0 * N + int64_t(nt) * OUT_N + pass * PN;
-      for (int c = tid; c < rows_valid * OCH; c += kThreads) {
-        const int r = c / OCH, ch = c % OCH;
-        *reinterpret_cast<u32x4*>(C + int64_t(r) * N + ch * 8) =
-            *reinterpret_cast<const u32x4*>(ct + r * PN + ch * 8);
+    } else {
+      constexpr int NOUT = KIND == kGatedSave ? 3 : 1;
+      constexpr int PN = OUT_N / EP;  // output columns per pass
+      constexpr int OCH = PN / 8;     // 16-byte chunks per output row of a pass
+      for (int o = 0; o < NOUT; ++o) {
+        // destination of output o: h (or the plain product), then g and u
+        uint16_t* dst = o == 0 ? g.c : g.aux_out;
+        const int64_t ld = o == 0 ? int64_t(N) : 2 * int64_t(N);
+        const int64_t col0 = int64_t(nt) * OUT_N + (o == 2 ? int64_t(N) : 0);
+        for (int pass = 0; pass < EP; ++pass) {
+          if (wn / (WAVES_N / EP) == pass) {
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+              for (int j = 0; j < HALF; ++j)
+#pragma unroll
+                for (int q = 0; q < 16; ++q) {
+                  const int r = wm * WROWS + i * 32 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
+                  const int col = wn * WCOL + j * 32 + (lane & 31);
+                  float v = acc[i][j][q];
+                  if constexpr (GATED) {
+                    const float up = acc[i][j + HALF][q];
+                    v = o == 0 ? silu(v) * up : o == 1 ? v : up;
+                  }
+                  ct[r * PN + col - pass * PN] = to_bf16(v);
+                }
+          }
+          __syncthreads();
+          uint16_t* C = dst + row0 * ld + col0 + pass * PN;
+          for (int c = tid; c < rows_valid * OCH; c += kThreads) {
+            const int r = c / OCH, ch = c % OCH;
+            *reinterpret_cast<u32x4*>(C + int64_t(r) * ld + ch * 8) =
+                *reinterpret_cast<const u32x4*>(ct + r * PN + ch * 8);
+          }
+          if (pass + 1 < EP || o + 1 < NOUT) __syncthreads();  // read out before the next write
+        }
       }
-      if (pass + 1 < EP) __syncthreads();  // pass read out before the next one is written
     }
     __syncthreads();  // the tile buffer is read out before the next tile's loads
   }
 }
 
-template <int BM, int BN, int BK, int STAGES, bool GATED, int TM>
+template <int BM, int BN, int BK, int STAGES, int KIND, int TM>
 hipError_t launch(const GemmArgs& a, hipStream_t s) {
-  grouped_gemm_kernel<BM, BN, BK, STAGES, GATED, TM><<<device_cu_count(), kThreads, 0, s>>>(a);
+  grouped_gemm_kernel<BM, BN, BK, STAGES, KIND, TM><<<device_cu_count(), kThreads, 0, s>>>(a);
   return hipGetLastError();
 }
 
@@ -373,19 +461,70 @@ hipError_t launch_gate_up(const void* x_perm, const int32_t* offsets, const int3
                           int e_loc, int64_t m_cap, int H, int I, const void* w1t,
                           const void* w3t, void* h, hipStream_t s) {
   (void)m_cap;
-  const GemmArgs a{static_cast<const uint16_t*>(x_perm), static_cast<const uint16_t*>(w1t),
-                   static_cast<const uint16_t*>(w3t), static_cast<uint16_t*>(h), offsets, counts,
-                   e_loc, I, H};
-  return launch<320, 256, 64, 2, true, 5>(a, s);  // I % 128 == 0: 128 output columns per tile
+  GemmArgs a{};
+  a.a = static_cast<const uint16_t*>(x_perm);
+  a.b0 = static_cast<const uint16_t*>(w1t);
+  a.b1 = static_cast<const uint16_t*>(w3t);
+  a.c = static_cast<uint16_t*>(h);
+  a.offsets = offsets, a.counts = counts, a.e_loc = e_loc, a.n = I, a.k = H, a.ldb = H;
+  return launch<320, 256, 64, 2, kGated, 5>(a, s);  // I % 128 == 0: 128 output columns per tile
+}
+
+hipError_t launch_gate_up_save(const void* x_perm, const int32_t* offsets, const int32_t* counts,
+                               int e_loc, int H, int I, const void* w1t, const void* w3t, void* h,
+                               void* gu, hipStream_t s) {
+  GemmArgs a{};
+  a.a = static_cast<const uint16_t*>(x_perm);
+  a.b0 = static_cast<const uint16_t*>(w1t);
+  a.b1 = static_cast<const uint16_t*>(w3t);
+  a.c = static_cast<uint16_t*>(h);
+  a.aux_out = static_cast<uint16_t*>(gu);
+  a.offsets = offsets, a.counts = counts, a.e_loc = e_loc, a.n = I, a.k = H, a.ldb = H;
+  return launch<320, 256, 64, 2, kGatedSave, 5>(a, s);
 }
 
 hipError_t launch_down(const void* h, const int32_t* offsets, const int32_t* counts, int e_loc,
                        int64_t m_cap, int I, int H, const void* w2t, void* y, hipStream_t s) {
   (void)m_cap;
-  const GemmArgs a{static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(w2t), nullptr,
-                   static_cast<uint16_t*>(y), offsets, counts, e_loc, H, I};
-  if (H % 256 == 0) return launch<320, 256, 64, 2, false, 5>(a, s);
-  return launch<256, 128, 64, 2, false, 2>(a, s);
+  GemmArgs a{};
+  a.a = static_cast<const uint16_t*>(h);
+  a.b0 = static_cast<const uint16_t*>(w2t);
+  a.c = static_cast<uint16_t*>(y);
+  a.offsets = offsets, a.counts = counts, a.e_loc = e_loc, a.n = H, a.k = I, a.ldb = I;
+  if (H % 256 == 0) return launch<320, 256, 64, 2, kPlain, 5>(a, s);
+  return launch<256, 128, 64, 2, kPlain, 2>(a, s);
+}
+
+// dh = dy W2^T reads W2 in its math orientation [E_loc, I, H]: for this
+// product that is already output-major (N = I rows of K = H).
+hipError_t launch_down_backward(const void* dy, const void* gu, const int32_t* offsets,
+                                const int32_t* counts, int e_loc, int I, int H, const void* w2,
+                                void* dgu, hipStream_t s) {
+  GemmArgs a{};
+  a.a = static_cast<const uint16_t*>(dy);
+  a.b0 = static_cast<const uint16_t*>(w2);
+  a.c = static_cast<uint16_t*>(dgu);
+  a.aux = static_cast<const uint16_t*>(gu);
+  a.offsets = offsets, a.counts = counts, a.e_loc = e_loc, a.n = I, a.k = H, a.ldb = H;
+  // 256 x 128 tiles: with 320-row tiles the SwiGLU-backward epilogue's
+  // registers spill inside the K loop
+  return launch<256, 128, 64, 2, kSwigluBwd, 2>(a, s);
+}
+
+// dx = [dg | du] [W1 | W3]^T: W1 and W3 in math orientation [E_loc, H, I] are
+// output-major for this product (N = H rows of I), one for each half of K = 2I.
+hipError_t launch_gate_up_backward(const void* dgu, const int32_t* offsets, const int32_t* counts,
+                                   int e_loc, int H, int I, const void* w1, const void* w3,
+                                   void* dx, hipStream_t s) {
+  GemmArgs a{};
+  a.a = static_cast<const uint16_t*>(dgu);
+  a.b0 = static_cast<const uint16_t*>(w1);
+  a.b1 = static_cast<const uint16_t*>(w3);
+  a.c = static_cast<uint16_t*>(dx);
+  a.offsets = offsets, a.counts = counts, a.e_loc = e_loc, a.n = H, a.k = 2 * I, a.ldb = I;
+  a.k_split = I;
+  if (H % 256 == 0) return launch<320, 256, 64, 2, kKSplit, 5>(a, s);
+  return launch<256, 128, 64, 2, kKSplit, 2>(a, s);
 }
 
 }  // namespace moe

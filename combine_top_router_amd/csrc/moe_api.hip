@@ -189,6 +189,44 @@ int32_t moe_grouped_swiglu(const void* x_perm_d, const int32_t* offsets_d,
                           w2t_d, y_d, stream);
 }
 
+int32_t moe_grouped_gate_up_save(const void* x_perm_d, const int32_t* offsets_d,
+                                 const int32_t* counts_d, int32_t num_local_experts,
+                                 int64_t m_cap, int32_t hidden, int32_t inter, const void* w1t_d,
+                                 const void* w3t_d, void* h_d, void* gu_d, void* stream) {
+  int32_t st = check_gemm(x_perm_d, offsets_d, counts_d, num_local_experts, m_cap, hidden, inter,
+                          w1t_d, w3t_d, h_d);
+  if (st == MOE_OK && (!gu_d || !aligned16(gu_d))) st = MOE_ERR_ARG;
+  if (st != MOE_OK) return st;
+  return status_of(moe::launch_gate_up_save(x_perm_d, offsets_d, counts_d, num_local_experts,
+                                            hidden, inter, w1t_d, w3t_d, h_d, gu_d,
+                                            as_stream(stream)));
+}
+
+int32_t moe_grouped_down_backward(const void* dy_d, const void* gu_d, const int32_t* offsets_d,
+                                  const int32_t* counts_d, int32_t num_local_experts,
+                                  int64_t m_cap, int32_t inter, int32_t hidden, const void* w2_d,
+                                  void* dgu_d, void* stream) {
+  int32_t st = check_gemm(dy_d, offsets_d, counts_d, num_local_experts, m_cap, hidden, inter,
+                          w2_d, w2_d, dgu_d);
+  if (st == MOE_OK && (!gu_d || !aligned16(gu_d))) st = MOE_ERR_ARG;
+  if (st != MOE_OK) return st;
+  return status_of(moe::launch_down_backward(dy_d, gu_d, offsets_d, counts_d, num_local_experts,
+                                             inter, hidden, w2_d, dgu_d, as_stream(stream)));
+}
+
+int32_t moe_grouped_gate_up_backward(const void* dgu_d, const int32_t* offsets_d,
+                                     const int32_t* counts_d, int32_t num_local_experts,
+                                     int64_t m_cap, int32_t hidden, int32_t inter,
+                                     const void* w1_d, const void* w3_d, void* dx_perm_d,
+                                     void* stream) {
+  const int32_t st = check_gemm(dgu_d, offsets_d, counts_d, num_local_experts, m_cap, inter,
+                                hidden, w1_d, w3_d, dx_perm_d);
+  if (st != MOE_OK) return st;
+  return status_of(moe::launch_gate_up_backward(dgu_d, offsets_d, counts_d, num_local_experts,
+                                                hidden, inter, w1_d, w3_d, dx_perm_d,
+                                                as_stream(stream)));
+}
+
 int32_t moe_combine(const void* y_d, int64_t y_rows, const int32_t* dst_row_d,
                     const float* topk_w_d, int64_t num_tokens, int32_t hidden, int32_t top_k,
                     void* out_d, void* stream) {

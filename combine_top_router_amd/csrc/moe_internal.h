@@ -26,6 +26,8 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+__device__ __forceinline__ float from_bf16(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
+
 __device__ __forceinline__ uint16_t to_bf16(float f) {
   return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
@@ -99,6 +101,15 @@ hipError_t launch_gate_up(const void* x_perm, const int32_t* offsets, const int3
                           const void* w3t, void* h, hipStream_t s);
 hipError_t launch_down(const void* h, const int32_t* offsets, const int32_t* counts, int e_loc,
                        int64_t m_cap, int I, int H, const void* w2t, void* y, hipStream_t s);
+hipError_t launch_gate_up_save(const void* x_perm, const int32_t* offsets, const int32_t* counts,
+                               int e_loc, int H, int I, const void* w1t, const void* w3t, void* h,
+                               void* gu, hipStream_t s);
+hipError_t launch_down_backward(const void* dy, const void* gu, const int32_t* offsets,
+                                const int32_t* counts, int e_loc, int I, int H, const void* w2,
+                                void* dgu, hipStream_t s);
+hipError_t launch_gate_up_backward(const void* dgu, const int32_t* offsets, const int32_t* counts,
+                                   int e_loc, int H, int I, const void* w1, const void* w3,
+                                   void* dx, hipStream_t s);
 
 int device_cu_count();
 

@@ -285,3 +285,54 @@ def route_backward(topk_idx: torch.Tensor, topk_w: torch.Tensor, grad_w: torch.T
         _ptr(topk_idx), _ptr(topk_w), _ptr(grad_w), T, num_experts, k, _ptr(out),
         _stream(out.device)))
     return out
+
+
+def grouped_gate_up_save(x_perm, offsets, counts, w1t, w3t, h=None, gu=None):
+    """(h, gu): h as grouped_gate_up, and gu [m_cap, 2I] = [x W1 | x W3] in bf16
+    for the backward."""
+    e_loc = _gemm_common(x_perm, offsets, counts)
+    m_cap, H = x_perm.shape
+    I = w1t.shape[1]
+    _need(w1t, "w1t", torch.bfloat16, (e_loc, I, H))
+    _need(w3t, "w3t", torch.bfloat16, (e_loc, I, H))
+    h = _empty((m_cap, I), torch.bfloat16, x_perm.device) if h is None else h
+    gu = _empty((m_cap, 2 * I), torch.bfloat16, x_perm.device) if gu is None else gu
+    _need(h, "h", torch.bfloat16, (m_cap, I))
+    _need(gu, "gu", torch.bfloat16, (m_cap, 2 * I))
+    check("moe_grouped_gate_up_save", lib().moe_grouped_gate_up_save(
+        _ptr(x_perm), _ptr(offsets), _ptr(counts), e_loc, m_cap, H, I, _ptr(w1t), _ptr(w3t),
+        _ptr(h), _ptr(gu), _stream(x_perm.device)))
+    return h, gu
+
+
+def grouped_down_backward(dy, gu, offsets, counts, w2, dgu=None):
+    """dgu [m_cap, 2I] = [dh u silu'(g) | dh silu(g)] with dh = dy W2^T; w2 is
+    the math-orientation [E_loc, I, H]."""
+    e_loc = _gemm_common(dy, offsets, counts)
+    m_cap, H = dy.shape
+    I = w2.shape[1]
+    _need(w2, "w2", torch.bfloat16, (e_loc, I, H))
+    _need(gu, "gu", torch.bfloat16, (m_cap, 2 * I))
+    dgu = _empty((m_cap, 2 * I), torch.bfloat16, dy.device) if dgu is None else dgu
+    _need(dgu, "dgu", torch.bfloat16, (m_cap, 2 * I))
+    check("moe_grouped_down_backward", lib().moe_grouped_down_backward(
+        _ptr(dy), _ptr(gu), _ptr(offsets), _ptr(counts), e_loc, m_cap, I, H, _ptr(w2), _ptr(dgu),
+        _stream(dy.device)))
+    return dgu
+
+
+def grouped_gate_up_backward(dgu, offsets, counts, w1, w3, dx=None):
+    """dx_perm [m_cap, H] = dg W1^T + du W3^T; w1, w3 are the math-orientation
+    [E_loc, H, I]."""
+    e_loc = _gemm_common(dgu, offsets, counts)
+    m_cap, I2 = dgu.shape
+    I = I2 // 2
+    H = w1.shape[1]
+    _need(w1, "w1", torch.bfloat16, (e_loc, H, I))
+    _need(w3, "w3", torch.bfloat16, (e_loc, H, I))
+    dx = _empty((m_cap, H), torch.bfloat16, dgu.device) if dx is None else dx
+    _need(dx, "dx_perm", torch.bfloat16, (m_cap, H))
+    check("moe_grouped_gate_up_backward", lib().moe_grouped_gate_up_backward(
+        _ptr(dgu), _ptr(offsets), _ptr(counts), e_loc, m_cap, H, I, _ptr(w1), _ptr(w3), _ptr(dx),
+        _stream(dgu.device)))
+    return dx

@@ -206,6 +206,46 @@ int32_t moe_grouped_swiglu(const void* x_perm_d, const int32_t* offsets_d,
                            void* h_d, void* y_d, void* stream);
 
 /*
+ * Training: the forward keeps the pre-activations, and the backward of the
+ * grouped SwiGLU experts produces the data gradient of x_perm. Training runs
+ * the grouped-GEMM path forward and backward and hands the expert gradients
+ * back in BF16 (xtuner PR #2056 "Integrate MoonEP dispatcher ...", section
+ * "Summary"). With g = x W1[e], u = x W3[e] (fp32 accumulators), for the rows
+ * [offsets[e], offsets[e] + counts[e]) of local expert e:
+ *
+ *   moe_grouped_gate_up_save:     h as moe_grouped_gate_up, and gu = [g | u] rounded to
+ *                                 bf16 (the two halves of each gu row)
+ *   moe_grouped_down_backward:    dh = dy W2[e]^T (fp32), then with g, u read from gu
+ *                                 dgu = [dh u silu'(g) | dh silu(g)] rounded to bf16,
+ *                                 silu'(g) = s (1 + g (1 - s)), s = 1 / (1 + e^-g)
+ *   moe_grouped_gate_up_backward: dx_perm = dg W1[e]^T + du W3[e]^T (one fp32 sum over
+ *                                 the 2I products), rounded to bf16
+ *
+ *   x_perm_d, dy_d, dx_perm_d [m_cap, H] bf16;  h_d [m_cap, I];  gu_d, dgu_d [m_cap, 2I]
+ *   w1t_d, w3t_d [E_loc, I, H] (moe_pack_weights layout, forward only)
+ *   w1_d, w3_d [E_loc, H, I], w2_d [E_loc, I, H]: the math-orientation weights, which
+ *   are already output-major for the backward products
+ * Rows outside the expert groups are neither read nor written. Limits as the
+ * forward calls (H and I multiples of 128).
+ */
+int32_t moe_grouped_gate_up_save(const void* x_perm_d, const int32_t* offsets_d,
+                                 const int32_t* counts_d, int32_t num_local_experts,
+                                 int64_t m_cap, int32_t hidden, int32_t inter,
+                                 const void* w1t_d, const void* w3t_d, void* h_d, void* gu_d,
+                                 void* stream);
+
+int32_t moe_grouped_down_backward(const void* dy_d, const void* gu_d, const int32_t* offsets_d,
+                                  const int32_t* counts_d, int32_t num_local_experts,
+                                  int64_t m_cap, int32_t inter, int32_t hidden,
+                                  const void* w2_d, void* dgu_d, void* stream);
+
+int32_t moe_grouped_gate_up_backward(const void* dgu_d, const int32_t* offsets_d,
+                                     const int32_t* counts_d, int32_t num_local_experts,
+                                     int64_t m_cap, int32_t hidden, int32_t inter,
+                                     const void* w1_d, const void* w3_d, void* dx_perm_d,
+                                     void* stream);
+
+/*
  * moe_combine -- fused weighted-sum restore.
  *
  * The fused restore of DeepSpeed PR #8847 ("AutoEP: support

@@ -1,5 +1,7 @@
 """GPU parity of the backward calls (moe_combine_backward, moe_permute_backward,
-moe_route_backward) against oracle/backward.py on the same seeded inputs.
+moe_route_backward, and the expert calls moe_grouped_gate_up_save,
+moe_grouped_down_backward, moe_grouped_gate_up_backward) against
+oracle/backward.py and oracle/experts.py on the same seeded inputs.
 
 Routing and layout come from the oracle (inputs never come from the HIP path);
 expert outputs and gradients from ``workloads.gen``. Bars:
@@ -11,7 +13,12 @@ expert outputs and gradients from ``workloads.gen``. Bars:
   a whole workload a relative L2 error vs fp64 of the FP32 class the pages
   report (8.4e-8 at hidden 6144; held to <= 5e-7);
 - routing gradient: within an fp32 bound of the fp64 formula, exact zeros on
-  unselected experts.
+  unselected experts;
+- expert backward: the saved pre-activations, dg/du and dx_perm within
+  max|gpu - oracle| / max|oracle| <= 1e-2 of the fp64 calculus per expert
+  group (the layer's bar: bf16 inputs, bf16 g/u/dg/du/dx roundings); the
+  saving forward's h bit-equal to the plain forward's; rows outside the
+  expert groups untouched.
 Small shapes are checked in full; the DeepSeek-V3 share and the pages' restore
 benchmark shape (8192 tokens, top-4 of 128 experts, hidden 6144) on all
 scores and on sampled rows.
@@ -157,3 +164,99 @@ def test_backward_argument_checks_launch_nothing():
     assert lib.moe_route_backward(None, None, None, 4, 8, 9, None, None) == 1
     # T * E past 2^32 entries is refused before any launch
     assert lib.moe_route_backward(None, None, None, 1 << 30, 16, 2, None, None) == 2
+
+
+# ---------------------------------------------------------------- experts
+
+from oracle import experts as oexperts  # noqa: E402
+
+EXPERT_SHAPES = {
+    # name: (config, local share, sample rows of at most this many experts)
+    "tiny": (workloads.get("tiny"), 1, None),
+    "small_h": (MoEConfig(name="small_h_bwd", num_tokens=600, hidden=384, num_experts=6,
+                          top_k=2, inter=128, ep_size=2, local_rank=1, align=64), 1, None),
+    "wide_i": (MoEConfig(name="wide_i_bwd", num_tokens=512, hidden=256, num_experts=4,
+                         top_k=2, inter=640, align=32), -1, None),
+    "deepseek_share": (workloads.get("deepseek_v3_ep8_share"), 0, 3),
+}
+REL = 1e-2  # max|gpu - oracle| / max|oracle| per checked expert group
+
+
+def _expert_inputs(name):
+    cfg, share, sample = EXPERT_SHAPES[name]
+    _, logits = workloads.gen.routing_inputs(cfg, "balanced", 0, device="cpu")
+    idx = oroute.select(logits.numpy(), cfg.top_k)
+    L = olayout.layout(idx, cfg.num_experts, cfg.ep_size, share, cfg.align)
+    m_cap = cfg.m_cap(share)
+    x_perm = workloads.gen.expert_outputs(cfg, m_cap, 1, device="cpu")  # stand-in rows
+    dy = workloads.gen.expert_outputs(cfg, m_cap, 2, device="cpu")
+    experts = list(cfg.local_experts(share))
+    w1, w3, w2 = workloads.gen.expert_weights(cfg, experts, 0, device="cpu")
+    return cfg, L, m_cap, x_perm, dy, (w1, w3, w2), sample
+
+
+def _groups(L, sample):
+    counts = L["local_counts"]
+    nz = [e for e in range(len(counts)) if counts[e] > 0]
+    if sample is not None:
+        rng = np.random.default_rng(5)
+        nz = sorted(rng.choice(nz, size=min(sample, len(nz)), replace=False).tolist())
+    return [(e, int(L["offsets"][e]), int(counts[e])) for e in nz]
+
+
+@pytest.mark.parametrize("name", list(EXPERT_SHAPES))
+def test_expert_backward(name):
+    announce("expert_backward", name)
+    cfg, L, m_cap, x_perm, dy, (w1, w3, w2), sample = _expert_inputs(name)
+    I = cfg.inter
+    off_d, cnt_d = i32(L["offsets"]), i32(L["local_counts"])
+    xd, dyd = x_perm.to(DEV), dy.to(DEV)
+    w1d, w3d, w2d = w1.to(DEV), w3.to(DEV), w2.to(DEV)
+    w1t, w3t = moe.ops.pack_weights(w1d), moe.ops.pack_weights(w3d)
+
+    sent = np.full((m_cap, 2 * I), SENTINEL, dtype=np.uint16)
+    gu = from_bits(sent)
+    dgu = from_bits(sent)
+    dx = from_bits(np.full((m_cap, cfg.hidden), SENTINEL, dtype=np.uint16))
+    h, _ = moe.ops.grouped_gate_up_save(xd, off_d, cnt_d, w1t, w3t, gu=gu)
+    h_plain = moe.ops.grouped_gate_up(xd, off_d, cnt_d, w1t, w3t)
+    moe.ops.grouped_down_backward(dyd, gu, off_d, cnt_d, w2d, dgu=dgu)
+    moe.ops.grouped_gate_up_backward(dgu, off_d, cnt_d, w1d, w3d, dx=dx)
+    torch.cuda.synchronize()
+
+    groups = _groups(L, sample)
+    rows = np.concatenate([np.arange(a, a + c) for _, a, c in groups])
+    # the saving forward computes h exactly as the plain one
+    np.testing.assert_array_equal(bits(h)[rows], bits(h_plain)[rows])
+    gu_b, dgu_b, dx_b = bits(gu), bits(dgu), bits(dx)
+    if sample is None:  # rows outside every expert group are never written
+        inside = np.zeros(m_cap, dtype=bool)
+        inside[rows] = True
+        assert (gu_b[~inside] == SENTINEL).all() and (dgu_b[~inside] == SENTINEL).all()
+        assert (dx_b[~inside] == SENTINEL).all()
+
+    for e, a, c in groups:
+        xs, dys = f64(x_perm[a:a + c]), f64(dy[a:a + c])
+        w1e, w3e, w2e = f64(w1[e]), f64(w3[e]), f64(w2[e])
+        gu_g = obf16_decode(gu_b[a:a + c])
+        dgu_g = obf16_decode(dgu_b[a:a + c])
+        g = xs @ w1e
+        u = xs @ w3e
+        assert relmax(gu_g[:, :I], g) <= REL and relmax(gu_g[:, I:], u) <= REL
+        s = 1.0 / (1.0 + np.exp(-g))
+        dh = dys @ w2e.T
+        assert relmax(dgu_g[:, :I], dh * u * (s * (1 + g * (1 - s)))) <= REL, e
+        assert relmax(dgu_g[:, I:], dh * g * s) <= REL, e
+        want = oexperts.swiglu_backward(xs, w1e, w3e, w2e, dys)[0]
+        got = obf16_decode(dx_b[a:a + c])
+        assert relmax(got, want) <= REL, (e, relmax(got, want))
+
+
+def obf16_decode(b):
+    from oracle import bf16 as _b
+    return _b.decode(b)
+
+
+def relmax(got, want):
+    den = np.abs(want).max()
+    return float(np.abs(np.asarray(got, np.float64) - want).max() / (den if den > 0 else 1.0))

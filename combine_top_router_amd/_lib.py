@@ -48,6 +48,8 @@ SIGNATURES = {
     "moe_grouped_gate_up_save": (_I32, [_P, _P, _P, _I32, _I64, _I32, _I32, _P, _P, _P, _P, _P]),
     "moe_grouped_down_backward": (_I32, [_P, _P, _P, _P, _I32, _I64, _I32, _I32, _P, _P, _P]),
     "moe_grouped_gate_up_backward": (_I32, [_P, _P, _P, _I32, _I64, _I32, _I32, _P, _P, _P, _P]),
+    "moe_grouped_gate_up_wgrad": (_I32, [_P, _P, _P, _P, _I32, _I64, _I32, _I32, _P, _P, _P]),
+    "moe_grouped_down_wgrad": (_I32, [_P, _P, _P, _P, _I32, _I64, _I32, _I32, _P, _P]),
     "moe_combine": (_I32, [_P, _I64, _P, _P, _I64, _I32, _I32, _P, _P]),
     "moe_combine_backward": (_I32, [_P, _P, _I64, _P, _P, _I64, _I32, _I32, _P, _P, _P]),
     "moe_permute_backward": (_I32, [_P, _I64, _P, _I64, _I32, _I32, _P, _P]),

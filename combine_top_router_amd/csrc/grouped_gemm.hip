@@ -86,37 +86,6 @@ struct GemmArgs {
   uint16_t* aux_out;       // kGatedSave: [rows, 2N] bf16 (out)
 };
 
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-
-// Buffer resource for a raw byte range [base, base + bytes): loads past the
-// end return zeros instead of touching memory.
-__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  i32x4 r;
-  r[0] = __builtin_amdgcn_readfirstlane(static_cast<int>(a & 0xffffffffu));
-  r[1] = __builtin_amdgcn_readfirstlane(static_cast<int>((a >> 32) & 0xffffu));  // stride 0
-  r[2] = __builtin_amdgcn_readfirstlane(static_cast<int>(bytes));               // num_records
-  r[3] = 0x00020000;  // raw 32-bit data format, no swizzle
-  return r;
-}
-
-// 16 bytes per lane, memory -> LDS through the buffer path, no register
-// staging: lane l's chunk lands at LDS byte lds_addr + 16*l. Issued through
-// inline assembly so that the compiler does not wait for these transfers
-// before unrelated LDS reads; the kernel waits for them itself (s_waitcnt
-// vmcnt + barrier) before reading the stage they fill. The instruction has
-// no register result.
-__device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t byte_off, uint32_t lds_addr) {
-  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(byte_off), "s"(rsrc),
-               "{m0}"(lds_addr)
-               : "memory");
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
 __device__ __forceinline__ float silu(float g) {
   return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
 }

@@ -227,6 +227,29 @@ int32_t moe_grouped_gate_up_backward(const void* dgu_d, const int32_t* offsets_d
                                                 as_stream(stream)));
 }
 
+int32_t moe_grouped_gate_up_wgrad(const void* x_perm_d, const void* dgu_d,
+                                  const int32_t* offsets_d, const int32_t* counts_d,
+                                  int32_t num_local_experts, int64_t m_cap, int32_t hidden,
+                                  int32_t inter, void* dw1_d, void* dw3_d, void* stream) {
+  const int32_t st = check_gemm(x_perm_d, offsets_d, counts_d, num_local_experts, m_cap, hidden,
+                                inter, dgu_d, dw1_d, dw3_d);
+  if (st != MOE_OK) return st;
+  return status_of(moe::launch_gate_up_wgrad(x_perm_d, dgu_d, offsets_d, counts_d,
+                                             num_local_experts, hidden, inter, dw1_d, dw3_d,
+                                             as_stream(stream)));
+}
+
+int32_t moe_grouped_down_wgrad(const void* h_d, const void* dy_d, const int32_t* offsets_d,
+                               const int32_t* counts_d, int32_t num_local_experts,
+                               int64_t m_cap, int32_t inter, int32_t hidden, void* dw2_d,
+                               void* stream) {
+  const int32_t st = check_gemm(h_d, offsets_d, counts_d, num_local_experts, m_cap, inter, hidden,
+                                dy_d, dy_d, dw2_d);
+  if (st != MOE_OK) return st;
+  return status_of(moe::launch_down_wgrad(h_d, dy_d, offsets_d, counts_d, num_local_experts,
+                                          inter, hidden, dw2_d, as_stream(stream)));
+}
+
 int32_t moe_combine(const void* y_d, int64_t y_rows, const int32_t* dst_row_d,
                     const float* topk_w_d, int64_t num_tokens, int32_t hidden, int32_t top_k,
                     void* out_d, void* stream) {

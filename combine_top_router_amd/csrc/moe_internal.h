@@ -48,6 +48,39 @@ __device__ __forceinline__ u32x4 pack8(const float (&f)[8]) {
   return v;
 }
 
+// ---- buffer loads straight into LDS (shared by the matrix-core kernels)
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer resource for a raw byte range [base, base + bytes): loads past the
+// end return zeros instead of touching memory.
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane(static_cast<int>(a & 0xffffffffu));
+  r[1] = __builtin_amdgcn_readfirstlane(static_cast<int>((a >> 32) & 0xffffu));  // stride 0
+  r[2] = __builtin_amdgcn_readfirstlane(static_cast<int>(bytes));               // num_records
+  r[3] = 0x00020000;  // raw 32-bit data format, no swizzle
+  return r;
+}
+
+// 16 bytes per lane, memory -> LDS through the buffer path, no register
+// staging: lane l's chunk lands at LDS byte lds_addr + 16*l. Issued through
+// inline assembly so that the compiler does not wait for these transfers
+// before unrelated LDS reads; the kernel waits for them itself (s_waitcnt
+// vmcnt + barrier) before reading the stage they fill. The instruction has
+// no register result.
+__device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t byte_off, uint32_t lds_addr) {
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(byte_off), "s"(rsrc),
+               "{m0}"(lds_addr)
+               : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 // A value every lane of the wave agrees on, moved to a scalar register.
 __device__ __forceinline__ int64_t uniform(int64_t v) {
   uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
@@ -110,6 +143,12 @@ hipError_t launch_down_backward(const void* dy, const void* gu, const int32_t* o
 hipError_t launch_gate_up_backward(const void* dgu, const int32_t* offsets, const int32_t* counts,
                                    int e_loc, int H, int I, const void* w1, const void* w3,
                                    void* dx, hipStream_t s);
+hipError_t launch_gate_up_wgrad(const void* x_perm, const void* dgu, const int32_t* offsets,
+                                const int32_t* counts, int e_loc, int H, int I, void* dw1,
+                                void* dw3, hipStream_t s);
+hipError_t launch_down_wgrad(const void* h, const void* dy, const int32_t* offsets,
+                             const int32_t* counts, int e_loc, int I, int H, void* dw2,
+                             hipStream_t s);
 
 int device_cu_count();
 

@@ -1,0 +1,257 @@
+// Weight gradients of the grouped SwiGLU experts on the matrix cores.
+//
+// Training hands the expert weight gradients back in BF16 after the grouped
+// GEMM backward (xtuner PR #2056 "Integrate MoonEP dispatcher ...", section
+// "Summary"; commit "extend grouped GEMM for dynamic expert gradients"). Per
+// local expert e with rows [offsets[e], offsets[e] + counts[e]):
+//
+//   C[m, n] = sum over the expert's rows r of A[r, m] * B[r, n]
+//     dW1 | dW3 = x_perm^T [dg | du]     (M = H, N = 2I, split at column I)
+//     dW2       = h^T dy                 (M = I, N = H)
+//
+// fp32 accumulation, one bf16 rounding. The reduction runs over the rows,
+// which are the slow dimension of both operands, so the MFMA fragments (8
+// consecutive k per lane) are transposed on the way out of LDS:
+//  * tiles land in LDS as they sit in memory, row k of the slice holding BM
+//    (or BN) contiguous values, through buffer_load ... lds (16 bytes a lane);
+//  * gfx950's ds_read_b64_tr_b16 gives each lane of a 16-lane group four
+//    values down a column: the group's lanes point at 4 rows x 4 column
+//    quads, and lane i receives column i of the 4 rows. Two such reads make
+//    the 8 consecutive k of one A (or B) fragment row;
+//  * within a row the 16-byte chunks are XOR-swizzled by 4 * (k % 4): the 32
+//    lanes of two groups then cover all 64 LDS banks.
+// Rows past the expert's count read as zeros through the buffer range of each
+// K slice (padding rows between experts hold stale data). An expert with no
+// rows gets a zero gradient. Workgroups are persistent; each XCD takes a
+// contiguous range of tile ids (expert-major), so the tiles of one expert,
+// which share both operands, sit behind the same L2.
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * kWave;
+constexpr int BK = 64;  // rows of the reduction per slice
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+struct WgradArgs {
+  const uint16_t* a;       // [rows, M] bf16
+  const uint16_t* b;       // [rows, N] bf16
+  uint16_t* out0;          // [E_loc, M, n_split] bf16
+  uint16_t* out1;          // [E_loc, M, N - n_split] bf16 (unused when n_split == N)
+  const int32_t* offsets;  // [E_loc + 1]
+  const int32_t* counts;   // [E_loc]
+  int e_loc, m, n, n_split;
+};
+
+// physical 16-byte chunk of logical chunk c in slice row k (an involution)
+__device__ __forceinline__ int wg_swz(int c, int k) { return c ^ ((k & 3) << 2); }
+
+__device__ __forceinline__ bf16x8 tr_pair(const char* p0, const char* p1) {
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p0);
+  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p1);
+  typedef short v8i16 __attribute__((ext_vector_type(8)));
+  const v8i16 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+template <int BM, int BN>
+__global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(WgradArgs g) {
+  constexpr int TM = 2;  // 32-row blocks of m per wavefront
+  constexpr int WAVES_M = BM / (32 * TM), WAVES_N = kWaves / WAVES_M;
+  constexpr int WCOL = BN / WAVES_N, TN = WCOL / 32;
+  constexpr int A_BYTES = BK * BM * 2, B_BYTES = BK * BN * 2, STAGE = A_BYTES + B_BYTES;
+  constexpr int A_CPR = BM / 8, B_CPR = BN / 8;          // 16-byte chunks per slice row
+  constexpr int A_RPL = 64 / A_CPR, B_RPL = 64 / B_CPR;  // slice rows per 1 KiB wave-load
+  constexpr int A_LOADS = A_BYTES / 1024 / kWaves, B_LOADS = B_BYTES / 1024 / kWaves;
+  static_assert(WAVES_M * WAVES_N == kWaves && TN >= 1 && WCOL % 32 == 0, "wavefront grid");
+  static_assert(A_LOADS * 1024 * kWaves == A_BYTES && B_LOADS * 1024 * kWaves == B_BYTES,
+                "whole wave-loads");
+  static_assert(BM * WCOL * 2 <= 2 * STAGE, "epilogue pass fits the stages");
+
+  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+
+  const int tid = threadIdx.x, lane = lane_id(), wid = tid / kWave;
+  const int wm = wid / WAVES_N, wn = wid % WAVES_N;
+  const int M = g.m, N = g.n;
+  const int MT = M / BM, NTL = N / BN, per_expert = MT * NTL;
+  const int total = g.e_loc * per_expert;
+  const int G = gridDim.x;
+  int slot = blockIdx.x;
+  if ((G & 7) == 0) slot = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
+  const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(smem));
+
+  // fragment-read coordinates of this lane: group of 16, row quad r, column quad q
+  const int grp = lane >> 4, fr = (lane >> 2) & 3, fq = lane & 3;
+
+  for (int tile = slot; tile < total; tile += G) {
+    const int e = tile / per_expert;
+    const int rem = tile - e * per_expert;
+    const int mt = rem / NTL, nt = rem - mt * NTL;
+    const int cnt = uniform(g.counts[e]);
+    const int64_t base = int64_t(uniform(g.offsets[e]));
+    const int KT = (cnt + BK - 1) / BK;
+    const int m0 = mt * BM, n0 = nt * BN;
+
+    // per-lane source offsets (bytes) of each wave-load inside a slice
+    uint32_t oa[A_LOADS], ob[B_LOADS];
+#pragma unroll
+    for (int i = 0; i < A_LOADS; ++i) {
+      const int kr = (wid + kWaves * i) * A_RPL + lane / A_CPR;
+      const int lc = wg_swz(lane % A_CPR, kr);
+      oa[i] = (uint32_t(kr) * uint32_t(M) + uint32_t(m0 + 8 * lc)) * 2u;
+    }
+#pragma unroll
+    for (int i = 0; i < B_LOADS; ++i) {
+      const int kr = (wid + kWaves * i) * B_RPL + lane / B_CPR;
+      const int lc = wg_swz(lane % B_CPR, kr);
+      ob[i] = (uint32_t(kr) * uint32_t(N) + uint32_t(n0 + 8 * lc)) * 2u;
+    }
+    auto issue = [&](int kt, int st) {
+      // the slice's buffer ranges end at the expert's last row
+      const int rows = min(BK, cnt - kt * BK);
+      const i32x4 ra = make_rsrc(g.a + (base + int64_t(kt) * BK) * M, uint32_t(rows) * uint32_t(M) * 2u);
+      const i32x4 rb = make_rsrc(g.b + (base + int64_t(kt) * BK) * N, uint32_t(rows) * uint32_t(N) * 2u);
+      const uint32_t sbase = lds0 + st * STAGE;
+#pragma unroll
+      for (int i = 0; i < A_LOADS; ++i) dma16(ra, oa[i], sbase + (wid + kWaves * i) * 1024);
+#pragma unroll
+      for (int i = 0; i < B_LOADS; ++i)
+        dma16(rb, ob[i], sbase + A_BYTES + (wid + kWaves * i) * 1024);
+    };
+
+    f32x16 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+
+    // fragments of the 16-wide step kk of a slice: row k = 16 kk + 8 (grp / 2) + fr
+    // (+4 for the second read), column 16 (grp % 2) + 4 fq within the 32-block
+    auto read_frags = [&](const char* sb, int kk, bf16x8 (&fa)[TM], bf16x8 (&fb)[TN]) {
+      const int k = kk * 16 + 8 * (grp >> 1) + fr;
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int c = (wm * 64 + i * 32 + 16 * (grp & 1) + 4 * fq);
+        const int off = 16 * wg_swz(c >> 3, k) + 8 * (fq & 1);
+        fa[i] = tr_pair(sb + k * (BM * 2) + off, sb + (k + 4) * (BM * 2) + off);
+      }
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int c = (wn * WCOL + j * 32 + 16 * (grp & 1) + 4 * fq);
+        const int off = 16 * wg_swz(c >> 3, k) + 8 * (fq & 1);
+        fb[j] = tr_pair(sb + A_BYTES + k * (BN * 2) + off, sb + A_BYTES + (k + 4) * (BN * 2) + off);
+      }
+    };
+    auto mfma = [&](const bf16x8 (&fa)[TM], const bf16x8 (&fb)[TN]) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    };
+
+    if (KT > 0) {
+      bf16x8 fa[2][TM], fb[2][TN];
+      issue(0, 0);
+      wait_vmcnt<0>();
+      __syncthreads();  // slice 0 visible
+      if (KT > 1) issue(1, 1);
+      read_frags(smem, 0, fa[0], fb[0]);
+      for (int kt = 0; kt < KT; ++kt) {
+        const char* sb = smem + (kt & 1) * STAGE;
+#pragma unroll
+        for (int kk = 0; kk < 3; ++kk) {
+          read_frags(sb, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
+          mfma(fa[kk & 1], fb[kk & 1]);
+        }
+        if (kt + 1 < KT) {
+          wait_vmcnt<0>();  // slice kt+1 landed (this wavefront's part)
+          __syncthreads();  // ... everyone's, and slice kt is read
+          if (kt + 2 < KT) issue(kt + 2, kt & 1);
+          read_frags(smem + ((kt + 1) & 1) * STAGE, 0, fa[0], fb[0]);
+        }
+        mfma(fa[1], fb[1]);
+      }
+    }
+    __syncthreads();  // the stages are free for the epilogue
+
+    // epilogue, one pass per wavefront column: bf16 tile [BM, WCOL] in LDS,
+    // then 16-byte row stores into dW1 / dW3 (or dW2)
+    constexpr int OCH = WCOL / 8;
+    uint16_t* ct = reinterpret_cast<uint16_t*>(smem);
+    for (int pass = 0; pass < WAVES_N; ++pass) {
+      if (wn == pass) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+              const int r = wm * 64 + i * 32 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
+              ct[r * WCOL + j * 32 + (lane & 31)] = to_bf16(acc[i][j][q]);
+            }
+      }
+      __syncthreads();
+      const int col = n0 + pass * WCOL;  // never straddles n_split (a multiple of 128)
+      const bool second = col >= g.n_split;
+      const int ld = second ? N - g.n_split : g.n_split;
+      uint16_t* dst = (second ? g.out1 : g.out0) + (int64_t(e) * M + m0) * ld +
+                      (second ? col - g.n_split : col);
+      for (int c = tid; c < BM * OCH; c += kThreads) {
+        const int r = c / OCH, ch = c % OCH;
+        *reinterpret_cast<u32x4*>(dst + int64_t(r) * ld + ch * 8) =
+            *reinterpret_cast<const u32x4*>(ct + r * WCOL + ch * 8);
+      }
+      __syncthreads();  // the pass is read out before the next one (or the next tile's loads)
+    }
+  }
+}
+
+template <int BM, int BN>
+hipError_t launch(const WgradArgs& a, hipStream_t s) {
+  wgrad_kernel<BM, BN><<<device_cu_count(), kThreads, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_any(const WgradArgs& a, hipStream_t s) {
+  if (a.m % 256 == 0 && a.n % 256 == 0) return launch<256, 256>(a, s);
+  if (a.m % 256 == 0) return launch<256, 128>(a, s);
+  if (a.n % 256 == 0) return launch<128, 256>(a, s);
+  return launch<128, 128>(a, s);
+}
+
+}  // namespace
+
+hipError_t launch_gate_up_wgrad(const void* x_perm, const void* dgu, const int32_t* offsets,
+                                const int32_t* counts, int e_loc, int H, int I, void* dw1,
+                                void* dw3, hipStream_t s) {
+  WgradArgs a{};
+  a.a = static_cast<const uint16_t*>(x_perm);
+  a.b = static_cast<const uint16_t*>(dgu);
+  a.out0 = static_cast<uint16_t*>(dw1);
+  a.out1 = static_cast<uint16_t*>(dw3);
+  a.offsets = offsets, a.counts = counts, a.e_loc = e_loc;
+  a.m = H, a.n = 2 * I, a.n_split = I;
+  return launch_any(a, s);
+}
+
+hipError_t launch_down_wgrad(const void* h, const void* dy, const int32_t* offsets,
+                             const int32_t* counts, int e_loc, int I, int H, void* dw2,
+                             hipStream_t s) {
+  WgradArgs a{};
+  a.a = static_cast<const uint16_t*>(h);
+  a.b = static_cast<const uint16_t*>(dy);
+  a.out0 = static_cast<uint16_t*>(dw2);
+  a.out1 = nullptr;
+  a.offsets = offsets, a.counts = counts, a.e_loc = e_loc;
+  a.m = I, a.n = H, a.n_split = H;
+  return launch_any(a, s);
+}
+
+}  // namespace moe

@@ -336,3 +336,33 @@ def grouped_gate_up_backward(dgu, offsets, counts, w1, w3, dx=None):
         _ptr(dgu), _ptr(offsets), _ptr(counts), e_loc, m_cap, H, I, _ptr(w1), _ptr(w3), _ptr(dx),
         _stream(dgu.device)))
     return dx
+
+
+def grouped_gate_up_wgrad(x_perm, dgu, offsets, counts, dw1=None, dw3=None):
+    """(dW1, dW3) [E_loc, H, I] bf16: x_perm_e^T dg_e and x_perm_e^T du_e."""
+    e_loc = _gemm_common(x_perm, offsets, counts)
+    m_cap, H = x_perm.shape
+    I = dgu.shape[1] // 2
+    _need(dgu, "dgu", torch.bfloat16, (m_cap, 2 * I))
+    dw1 = _empty((e_loc, H, I), torch.bfloat16, x_perm.device) if dw1 is None else dw1
+    dw3 = _empty((e_loc, H, I), torch.bfloat16, x_perm.device) if dw3 is None else dw3
+    _need(dw1, "dw1", torch.bfloat16, (e_loc, H, I))
+    _need(dw3, "dw3", torch.bfloat16, (e_loc, H, I))
+    check("moe_grouped_gate_up_wgrad", lib().moe_grouped_gate_up_wgrad(
+        _ptr(x_perm), _ptr(dgu), _ptr(offsets), _ptr(counts), e_loc, m_cap, H, I, _ptr(dw1),
+        _ptr(dw3), _stream(x_perm.device)))
+    return dw1, dw3
+
+
+def grouped_down_wgrad(h, dy, offsets, counts, dw2=None):
+    """dW2 [E_loc, I, H] bf16: h_e^T dy_e."""
+    e_loc = _gemm_common(h, offsets, counts)
+    m_cap, I = h.shape
+    H = dy.shape[1]
+    _need(dy, "dy", torch.bfloat16, (m_cap, H))
+    dw2 = _empty((e_loc, I, H), torch.bfloat16, h.device) if dw2 is None else dw2
+    _need(dw2, "dw2", torch.bfloat16, (e_loc, I, H))
+    check("moe_grouped_down_wgrad", lib().moe_grouped_down_wgrad(
+        _ptr(h), _ptr(dy), _ptr(offsets), _ptr(counts), e_loc, m_cap, I, H, _ptr(dw2),
+        _stream(h.device)))
+    return dw2

@@ -246,6 +246,31 @@ int32_t moe_grouped_gate_up_backward(const void* dgu_d, const int32_t* offsets_d
                                      void* stream);
 
 /*
+ * Weight gradients of the grouped experts (BF16 out, fp32 accumulation over
+ * the expert's rows; xtuner PR #2056, section "Summary", and its commit
+ * "extend grouped GEMM for dynamic expert gradients"):
+ *
+ *   moe_grouped_gate_up_wgrad:  dW1[e] = x_perm_e^T dg_e,  dW3[e] = x_perm_e^T du_e
+ *   moe_grouped_down_wgrad:     dW2[e] = h_e^T dy_e
+ *
+ * where _e is the expert's rows [offsets[e], offsets[e] + counts[e]) and
+ * dgu = [dg | du] is moe_grouped_down_backward's output. An expert without
+ * rows gets a zero gradient.
+ *   dw1_d, dw3_d [E_loc, H, I] bf16 (out);  dw2_d [E_loc, I, H] bf16 (out)
+ *   (the math orientation of the weights)
+ * Limits as the forward calls.
+ */
+int32_t moe_grouped_gate_up_wgrad(const void* x_perm_d, const void* dgu_d,
+                                  const int32_t* offsets_d, const int32_t* counts_d,
+                                  int32_t num_local_experts, int64_t m_cap, int32_t hidden,
+                                  int32_t inter, void* dw1_d, void* dw3_d, void* stream);
+
+int32_t moe_grouped_down_wgrad(const void* h_d, const void* dy_d, const int32_t* offsets_d,
+                               const int32_t* counts_d, int32_t num_local_experts,
+                               int64_t m_cap, int32_t inter, int32_t hidden, void* dw2_d,
+                               void* stream);
+
+/*
  * moe_combine -- fused weighted-sum restore.
  *
  * The fused restore of DeepSpeed PR #8847 ("AutoEP: support

@@ -14,9 +14,9 @@ expert outputs and gradients from ``workloads.gen``. Bars:
   report (8.4e-8 at hidden 6144; held to <= 5e-7);
 - routing gradient: within an fp32 bound of the fp64 formula, exact zeros on
   unselected experts;
-- expert backward: the saved pre-activations, dg/du and dx_perm within
-  max|gpu - oracle| / max|oracle| <= 1e-2 of the fp64 calculus per expert
-  group (the layer's bar: bf16 inputs, bf16 g/u/dg/du/dx roundings); the
+- expert backward: the saved pre-activations, dg/du, dx_perm and the weight
+  gradients dW1, dW3, dW2 within max|gpu - oracle| / max|oracle| <= 1e-2 of
+  the fp64 calculus per expert group (the layer's bar: bf16 inputs, bf16 g/u/dg/du/dx roundings); the
   saving forward's h bit-equal to the plain forward's; rows outside the
   expert groups untouched.
 Small shapes are checked in full; the DeepSeek-V3 share and the pages' restore
@@ -178,13 +178,19 @@ EXPERT_SHAPES = {
     "wide_i": (MoEConfig(name="wide_i_bwd", num_tokens=512, hidden=256, num_experts=4,
                          top_k=2, inter=640, align=32), -1, None),
     "deepseek_share": (workloads.get("deepseek_v3_ep8_share"), 0, 3),
+    # 64 tokens, top-1 of 32 experts under severe skew: several experts get no
+    # rows and must come back with zero weight gradients
+    "empty_experts": (MoEConfig(name="empty_bwd", num_tokens=64, hidden=128, num_experts=32,
+                                top_k=1, inter=128, align=16), -1, None),
 }
+EXPERT_DIST = {"empty_experts": "severe"}
 REL = 1e-2  # max|gpu - oracle| / max|oracle| per checked expert group
 
 
 def _expert_inputs(name):
     cfg, share, sample = EXPERT_SHAPES[name]
-    _, logits = workloads.gen.routing_inputs(cfg, "balanced", 0, device="cpu")
+    _, logits = workloads.gen.routing_inputs(cfg, EXPERT_DIST.get(name, "balanced"), 0,
+                                             device="cpu")
     idx = oroute.select(logits.numpy(), cfg.top_k)
     L = olayout.layout(idx, cfg.num_experts, cfg.ep_size, share, cfg.align)
     m_cap = cfg.m_cap(share)
@@ -222,6 +228,8 @@ def test_expert_backward(name):
     h_plain = moe.ops.grouped_gate_up(xd, off_d, cnt_d, w1t, w3t)
     moe.ops.grouped_down_backward(dyd, gu, off_d, cnt_d, w2d, dgu=dgu)
     moe.ops.grouped_gate_up_backward(dgu, off_d, cnt_d, w1d, w3d, dx=dx)
+    dw1, dw3 = moe.ops.grouped_gate_up_wgrad(xd, dgu, off_d, cnt_d)
+    dw2 = moe.ops.grouped_down_wgrad(h, dyd, off_d, cnt_d)
     torch.cuda.synchronize()
 
     groups = _groups(L, sample)
@@ -247,9 +255,18 @@ def test_expert_backward(name):
         dh = dys @ w2e.T
         assert relmax(dgu_g[:, :I], dh * u * (s * (1 + g * (1 - s)))) <= REL, e
         assert relmax(dgu_g[:, I:], dh * g * s) <= REL, e
-        want = oexperts.swiglu_backward(xs, w1e, w3e, w2e, dys)[0]
+        want, wd1, wd3, wd2 = oexperts.swiglu_backward(xs, w1e, w3e, w2e, dys)
         got = obf16_decode(dx_b[a:a + c])
         assert relmax(got, want) <= REL, (e, relmax(got, want))
+        for name_, gpu, ref in (("dW1", dw1, wd1), ("dW3", dw3, wd3), ("dW2", dw2, wd2)):
+            r = relmax(f64(gpu[e]), ref)
+            assert r <= REL, (name_, e, r)
+    # experts without rows get exactly zero weight gradients
+    if name == "empty_experts":
+        assert (L["local_counts"] == 0).any()
+    for e in np.nonzero(L["local_counts"] == 0)[0]:
+        for gpu in (dw1, dw3, dw2):
+            assert not bits(gpu[int(e)]).any()
 
 
 def obf16_decode(b):

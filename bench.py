@@ -45,7 +45,7 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true",
-                    help="skip timing the backward calls (combine, permute, routing)")
+                    help="skip timing the backward calls")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for the CPU baseline sample")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -145,35 +145,56 @@ def cpu_baseline(cfg, dist, layer_args, budget_s):
                        f"{len(os.sched_getaffinity(0))} host cores visible")}
 
 
-def time_backward(args, cfg, layer, moe, stream, t_loc, n_loc):
+def time_backward(args, cfg, layer, moe, stream, t_loc, n_loc, weights):
     """Per-call times of the backward calls on this step's routing and rows,
-    after the forward timing (not part of the step or of ``value``). The
-    permute gradient's input is a stand-in buffer of the x_perm shape: the
-    expert backward that would produce it is not part of this library."""
+    after the forward timing (not part of the step or of ``value``): the
+    forward gate/up that also keeps the pre-activations, then the chain
+    combine -> routing -> down -> gate/up (data and weight gradients) ->
+    permute, each call fed by the one before it."""
     import numpy as np
     import torch
 
     import workloads
 
-    T, H, E, k = cfg.num_tokens, cfg.hidden, cfg.num_experts, cfg.top_k
+    T, H, E, k, I = cfg.num_tokens, cfg.hidden, cfg.num_experts, cfg.top_k, cfg.inter
     dev = layer.y.device
+    w1, w3, w2 = weights
+    L = layer.L
+    e_loc = w1.shape[0]
     G = workloads.gen.output_gradient(cfg, args.seed, device=dev)
     gy = torch.zeros_like(layer.y)
     gw = torch.empty((T, k), dtype=torch.float32, device=dev)
-    gx = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
     gl = torch.empty((T, E), dtype=torch.float32, device=dev)
-    dst = layer.L.dst_row
+    gu = torch.empty((layer.m_cap, 2 * I), dtype=torch.bfloat16, device=dev)
+    dgu = torch.empty_like(gu)
+    dxp = torch.empty_like(layer.x_perm)
+    gx = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    dw1 = torch.empty((e_loc, H, I), dtype=torch.bfloat16, device=dev)
+    dw3 = torch.empty_like(dw1)
+    dw2 = torch.empty((e_loc, I, H), dtype=torch.bfloat16, device=dev)
+    dst, off, cnt = L.dst_row, L.offsets, L.local_counts
+    nhi = float(n_loc) * H * I
     calls = [
+        ("gate_up_save", lambda: moe.ops.grouped_gate_up_save(
+            layer.x_perm, off, cnt, layer.w1t, layer.w3t, layer.h, gu), "mfma", 4 * nhi),
         ("combine_backward", lambda: moe.ops.combine_backward(G, layer.y, dst, layer.topk_w, gy, gw),
-         t_loc * H * 2 + 2 * n_loc * H * 2 + T * k * 12),
-        ("permute_backward", lambda: moe.ops.permute_backward(gy, dst, gx),
-         n_loc * H * 2 + T * H * 2 + T * k * 4),
+         "hbm", t_loc * H * 2 + 2 * n_loc * H * 2 + T * k * 12),
         ("route_backward", lambda: moe.ops.route_backward(layer.topk_idx, layer.topk_w, gw, E, gl),
-         T * E * 4 + T * k * 12),
+         "hbm", T * E * 4 + T * k * 12),
+        ("down_backward", lambda: moe.ops.grouped_down_backward(gy, gu, off, cnt, w2, dgu),
+         "mfma", 2 * nhi),
+        ("down_wgrad", lambda: moe.ops.grouped_down_wgrad(layer.h, gy, off, cnt, dw2),
+         "mfma", 2 * nhi),
+        ("gate_up_backward", lambda: moe.ops.grouped_gate_up_backward(dgu, off, cnt, w1, w3, dxp),
+         "mfma", 4 * nhi),
+        ("gate_up_wgrad", lambda: moe.ops.grouped_gate_up_wgrad(layer.x_perm, dgu, off, cnt, dw1, dw3),
+         "mfma", 4 * nhi),
+        ("permute_backward", lambda: moe.ops.permute_backward(dxp, dst, gx),
+         "hbm", n_loc * H * 2 + T * H * 2 + T * k * 4),
     ]
     reps = max(3, args.steps)
     out = {}
-    for name, run, nbytes in calls:
+    for name, run, bound, amount in calls:
         for _ in range(3):
             run()
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
@@ -186,9 +207,14 @@ def time_backward(args, cfg, layer, moe, stream, t_loc, n_loc):
             ev[r + 1].record(stream)
         torch.cuda.synchronize()
         ms = float(np.mean([ev[r].elapsed_time(ev[r + 1]) for r in range(reps)]))
-        gbs = nbytes / (ms * 1e-3) / 1e9
-        out[name] = {"ms": round(ms, 4), "bound": "hbm", "GB/s": round(gbs, 1),
-                     "frac": round(gbs / PEAK_HBM_GBS, 4), "bytes": int(nbytes)}
+        if bound == "hbm":
+            ach = amount / (ms * 1e-3) / 1e9
+            out[name] = {"ms": round(ms, 4), "bound": "hbm", "GB/s": round(ach, 1),
+                         "frac": round(ach / PEAK_HBM_GBS, 4), "bytes": int(amount)}
+        else:
+            ach = amount / (ms * 1e-3) / 1e12
+            out[name] = {"ms": round(ms, 4), "bound": "mfma", "TFLOP/s": round(ach, 1),
+                         "frac": round(ach / PEAK_BF16_TFLOPS, 4), "flops": amount}
     return out
 
 
@@ -293,7 +319,7 @@ def main():
                 "unit": "GB/s", "frac": d["frac"], "traffic": traffic}
 
     backward = None if args.no_backward else time_backward(args, cfg, layer, moe, stream,
-                                                            t_loc, n_loc)
+                                                            t_loc, n_loc, (w1, w3, w2))
 
     cpu = None
     if not args.no_cpu_baseline:

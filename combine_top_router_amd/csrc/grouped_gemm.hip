@@ -346,7 +346,9 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
           *reinterpret_cast<u32x4*>(ut + r * PN + ch * 8) = *reinterpret_cast<const u32x4*>(src + N);
         }
         __syncthreads();
-        for (int o = 0; o < 2; ++o) {
+        // output O (compile time): dg, then du
+        auto emit = [&](auto o_tag) __attribute__((always_inline)) {
+          constexpr int O = decltype(o_tag)::value;
           if (wn == pass) {
 #pragma unroll
             for (int i = 0; i < TM; ++i)
@@ -360,31 +362,36 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
                   const float dh = acc[i][j][q];
                   const float gg = from_bf16(gt[r * PN + col]);
                   const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-gg));
-                  const float v = o == 0 ? dh * from_bf16(ut[r * PN + col]) *
-                                               (sg * (1.0f + gg * (1.0f - sg)))
-                                         : dh * (gg * sg);
+                  float v;
+                  if constexpr (O == 0)
+                    v = dh * from_bf16(ut[r * PN + col]) * (sg * (1.0f + gg * (1.0f - sg)));
+                  else
+                    v = dh * (gg * sg);
                   ct[r * PN + col] = to_bf16(v);
                 }
           }
           __syncthreads();
-          uint16_t* C = g.c + row0 * 2 * int64_t(N) + o * int64_t(N) + cb;
+          uint16_t* C = g.c + row0 * 2 * int64_t(N) + O * int64_t(N) + cb;
           for (int c = tid; c < rows_valid * OCH; c += kThreads) {
             const int r = c / OCH, ch = c % OCH;
             *reinterpret_cast<u32x4*>(C + int64_t(r) * 2 * N + ch * 8) =
                 *reinterpret_cast<const u32x4*>(ct + r * PN + ch * 8);
           }
           __syncthreads();  // ct (and, after du, gt/ut) read out before the next write
-        }
+        };
+        emit(std::integral_constant<int, 0>{});
+        emit(std::integral_constant<int, 1>{});
       }
     } else {
       constexpr int NOUT = KIND == kGatedSave ? 3 : 1;
       constexpr int PN = OUT_N / EP;  // output columns per pass
       constexpr int OCH = PN / 8;     // 16-byte chunks per output row of a pass
-      for (int o = 0; o < NOUT; ++o) {
-        // destination of output o: h (or the plain product), then g and u
-        uint16_t* dst = o == 0 ? g.c : g.aux_out;
-        const int64_t ld = o == 0 ? int64_t(N) : 2 * int64_t(N);
-        const int64_t col0 = int64_t(nt) * OUT_N + (o == 2 ? int64_t(N) : 0);
+      // output O (compile time): h (or the plain product), then g and u
+      auto emit = [&](auto o_tag) __attribute__((always_inline)) {
+        constexpr int O = decltype(o_tag)::value;
+        uint16_t* dst = O == 0 ? g.c : g.aux_out;
+        const int64_t ld = O == 0 ? int64_t(N) : 2 * int64_t(N);
+        const int64_t col0 = int64_t(nt) * OUT_N + (O == 2 ? int64_t(N) : 0);
         for (int pass = 0; pass < EP; ++pass) {
           if (wn / (WAVES_N / EP) == pass) {
 #pragma unroll
@@ -397,8 +404,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
                   const int col = wn * WCOL + j * 32 + (lane & 31);
                   float v = acc[i][j][q];
                   if constexpr (GATED) {
-                    const float up = acc[i][j + HALF][q];
-                    v = o == 0 ? silu(v) * up : o == 1 ? v : up;
+                    if constexpr (O == 0) v = silu(v) * acc[i][j + HALF][q];
+                    else if constexpr (O == 2) v = acc[i][j + HALF][q];
                   }
                   ct[r * PN + col - pass * PN] = to_bf16(v);
                 }
@@ -410,8 +417,13 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
             *reinterpret_cast<u32x4*>(C + int64_t(r) * ld + ch * 8) =
                 *reinterpret_cast<const u32x4*>(ct + r * PN + ch * 8);
           }
-          if (pass + 1 < EP || o + 1 < NOUT) __syncthreads();  // read out before the next write
+          if (pass + 1 < EP || O + 1 < NOUT) __syncthreads();  // read out before the next write
         }
+      };
+      emit(std::integral_constant<int, 0>{});
+      if constexpr (NOUT > 1) {
+        emit(std::integral_constant<int, 1>{});
+        emit(std::integral_constant<int, 2>{});
       }
     }
     __syncthreads();  // the tile buffer is read out before the next tile's loads

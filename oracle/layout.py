@@ -124,3 +124,42 @@ def layout(topk_idx, num_experts: int, ep_size: int = 1, local_rank: int = -1,
         "num_local": el,
         "m_cap": int(m_cap),
     }
+
+
+def dispatch_layout(topk_idx, num_experts: int, ep_size: int) -> dict:
+    """Per-token, per-destination-rank layout of a deduplicated dispatch, as
+    int32 / uint8 numpy arrays.
+
+    DeepEP computes, before dispatching, the tokens per rank, tokens per
+    expert and a token-in-rank table from ``topk_idx`` and the expert count
+    (DeepEP issue #272, the maintainer's example: get_dispatch_layout returns
+    num_tokens_per_rank, num_tokens_per_expert and is_token_in_rank, which
+    the dispatch then consumes). The pages print only the names; the reading
+    taken is the plain one: a token is sent once to each rank that holds at
+    least one of its experts, whatever the number of its slots there.
+
+    is_token_in_rank     [T, ep] uint8   1 if some slot of t maps to an expert of rank r
+    num_tokens_per_rank  [ep]            column sums of is_token_in_rank
+    num_tokens_per_expert[E]             assignments per expert (ids outside [0, E) skipped)
+    token_rank_pos       [T, ep]         position of t among the tokens rank r receives,
+                                         in token order; -1 where t is not sent to r
+
+    Rank r holds the experts [r*E/ep, (r+1)*E/ep) (one GPU standing for ep
+    virtual ranks, as in ``layout``)."""
+    idx = np.asarray(topk_idx, dtype=np.int64)
+    T, k = idx.shape
+    el = num_experts // ep_size
+    valid = (idx >= 0) & (idx < num_experts)
+    in_rank = np.zeros((T, ep_size), dtype=bool)
+    for s in range(k):
+        m = valid[:, s]
+        in_rank[np.nonzero(m)[0], idx[m, s] // el] = True
+    per_rank = in_rank.sum(axis=0)
+    per_expert = np.bincount(idx[valid], minlength=num_experts)
+    pos = np.where(in_rank, np.cumsum(in_rank, axis=0) - 1, -1)
+    return {
+        "is_token_in_rank": in_rank.astype(np.uint8),
+        "num_tokens_per_rank": per_rank.astype(np.int32),
+        "num_tokens_per_expert": per_expert.astype(np.int32),
+        "token_rank_pos": pos.astype(np.int32),
+    }

@@ -213,3 +213,58 @@ def test_skew_distributions_skew():
     assert spread["balanced"] < spread["mild"] < spread["severe"]
     hot = workloads.gen.routing_bias(cfg, "severe").numpy() > 0
     assert counts["severe"][hot].min() > counts["severe"][~hot].max()
+
+
+# ---------------------------------------------------------------- dedup layout
+
+def _brute_dispatch_layout(idx, E, ep):
+    el = E // ep
+    T, k = len(idx), len(idx[0])
+    in_rank = [[0] * ep for _ in range(T)]
+    for t in range(T):
+        for s in range(k):
+            e = idx[t][s]
+            if 0 <= e < E:
+                in_rank[t][e // el] = 1
+    pos = [[-1] * ep for _ in range(T)]
+    count = [0] * ep
+    for t in range(T):
+        for r in range(ep):
+            if in_rank[t][r]:
+                pos[t][r] = count[r]
+                count[r] += 1
+    per_expert = [0] * E
+    for row in idx:
+        for e in row:
+            if 0 <= e < E:
+                per_expert[e] += 1
+    return in_rank, count, per_expert, pos
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2, 3])
+def test_dispatch_layout_matches_brute_force(seed):
+    rng = np.random.default_rng(seed)
+    E, ep, k = 12, 4, 3
+    T = 40
+    idx = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+    idx[rng.random(idx.shape) < 0.05] = E + 3  # a few out-of-range ids are skipped
+    got = olayout.dispatch_layout(idx, E, ep)
+    in_rank, count, per_expert, pos = _brute_dispatch_layout(idx.tolist(), E, ep)
+    np.testing.assert_array_equal(got["is_token_in_rank"], np.array(in_rank, dtype=np.uint8))
+    np.testing.assert_array_equal(got["num_tokens_per_rank"], count)
+    np.testing.assert_array_equal(got["num_tokens_per_expert"], per_expert)
+    np.testing.assert_array_equal(got["token_rank_pos"], pos)
+
+
+def test_dispatch_layout_worked_example(worked_example):
+    # the golden 4-token example: experts 0-1 on rank 0, 2-3 on rank 1
+    g = worked_example
+    idx = np.array(g["topk_idx"], dtype=np.int32)  # [[0,2],[2,3],[1,3],[0,2]]
+    got = olayout.dispatch_layout(idx, 4, 2)
+    # t0 -> ranks 0 and 1; t1 -> rank 1 only (two slots there, sent once); t2 -> both; t3 -> both
+    np.testing.assert_array_equal(got["is_token_in_rank"], [[1, 1], [0, 1], [1, 1], [1, 1]])
+    np.testing.assert_array_equal(got["num_tokens_per_rank"], [3, 4])
+    np.testing.assert_array_equal(got["token_rank_pos"], [[0, 0], [-1, 1], [1, 2], [2, 3]])
+    np.testing.assert_array_equal(got["num_tokens_per_expert"], g["expert_counts"])
+    # a token never counts more than once per rank, and at most min(k, ep) times overall
+    assert got["is_token_in_rank"].sum(axis=1).max() <= 2

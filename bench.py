@@ -146,11 +146,12 @@ def cpu_baseline(cfg, dist, layer_args, budget_s):
 
 
 def time_backward(args, cfg, layer, moe, stream, t_loc, n_loc, weights):
-    """Per-call times of the backward calls on this step's routing and rows,
-    after the forward timing (not part of the step or of ``value``): the
-    forward gate/up that also keeps the pre-activations, then the chain
+    """Per-call times of the calls outside the step, on this step's routing
+    and rows, after the forward timing (not part of ``value``): the forward
+    gate/up that also keeps the pre-activations, then the backward chain
     combine -> routing -> down -> gate/up (data and weight gradients) ->
-    permute, each call fed by the one before it."""
+    permute, each call fed by the one before it, and the per-rank
+    deduplicated dispatch layout."""
     import numpy as np
     import torch
 
@@ -173,6 +174,7 @@ def time_backward(args, cfg, layer, moe, stream, t_loc, n_loc, weights):
     dw3 = torch.empty_like(dw1)
     dw2 = torch.empty((e_loc, I, H), dtype=torch.bfloat16, device=dev)
     dst, off, cnt = L.dst_row, L.offsets, L.local_counts
+    dl_ep = max(cfg.ep_size, 8) if E % max(cfg.ep_size, 8) == 0 else cfg.ep_size
     nhi = float(n_loc) * H * I
     calls = [
         ("gate_up_save", lambda: moe.ops.grouped_gate_up_save(
@@ -191,6 +193,10 @@ def time_backward(args, cfg, layer, moe, stream, t_loc, n_loc, weights):
          "mfma", 4 * nhi),
         ("permute_backward", lambda: moe.ops.permute_backward(dxp, dst, gx),
          "hbm", n_loc * H * 2 + T * H * 2 + T * k * 4),
+        # the per-rank deduplicated layout (over the workload's ep virtual
+        # ranks, at least 8): T*k ids read, the [T, ep] table and positions written
+        ("dispatch_layout", lambda: moe.ops.dispatch_layout(layer.topk_idx, E, dl_ep),
+         "hbm", T * k * 4 + T * dl_ep * 5),
     ]
     reps = max(3, args.steps)
     out = {}

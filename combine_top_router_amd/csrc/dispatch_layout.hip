@@ -1,0 +1,145 @@
+// Per-rank deduplicated dispatch layout.
+//
+// DeepEP computes, from topk_idx and the expert count and before any data
+// moves, the tokens per rank, the tokens per expert and a token-in-rank
+// table that its dispatch consumes (DeepEP issue #272, the maintainer's
+// example around get_dispatch_layout). A token goes once to each rank that
+// holds at least one of its experts; rank r holds experts
+// [r*E/ep, (r+1)*E/ep). Outputs:
+//   is_token_in_rank [T, ep] uint8, num_tokens_per_rank [ep],
+//   num_tokens_per_expert [E], token_rank_pos [T, ep] (position of t among
+//   the tokens rank r receives, in token order; -1 if not sent).
+//
+// Three launches on one stream, one thread per token:
+//   count  per tile of 256 tokens: each rank's tokens (wavefront ballots over
+//          the token's rank mask) and an LDS histogram of expert ids;
+//   scan   one workgroup: per-rank exclusive scan over tiles, per-expert sums;
+//   place  per tile: the token's position = tile base + tokens of the tile
+//          before it (ballot prefix within the wavefront + earlier wavefronts).
+// Integer sums only, no atomics across workgroups: the result does not
+// depend on scheduling.
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kTile = 256;  // tokens per workgroup, one per thread
+constexpr int kTileWaves = kTile / kWave;
+
+struct DlArgs {
+  const int32_t* idx;
+  int64_t T;
+  int E, k, ep, el;
+  int tiles;
+  int32_t* tile_rank;    // [tiles, ep]  counts, then exclusive bases
+  int32_t* tile_expert;  // [tiles, E]
+};
+
+__device__ __forceinline__ uint64_t rank_mask(const DlArgs& a, int64_t t) {
+  uint64_t m = 0;
+  if (t < a.T) {
+    for (int s = 0; s < a.k; ++s) {
+      const int e = a.idx[t * a.k + s];
+      if (static_cast<unsigned>(e) < static_cast<unsigned>(a.E)) m |= 1ull << (e / a.el);
+    }
+  }
+  return m;
+}
+
+__global__ __launch_bounds__(kTile) void dl_count_kernel(DlArgs a) {
+  __shared__ int32_t hist[1024];
+  __shared__ int32_t wave_cnt[kTileWaves][64];
+  const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
+  const int tile = blockIdx.x;
+  for (int e = tid; e < a.E; e += kTile) hist[e] = 0;
+  __syncthreads();
+  const int64_t t = int64_t(tile) * kTile + tid;
+  if (t < a.T)
+    for (int s = 0; s < a.k; ++s) {
+      const int e = a.idx[t * a.k + s];
+      if (static_cast<unsigned>(e) < static_cast<unsigned>(a.E)) atomicAdd(&hist[e], 1);
+    }
+  const uint64_t m = rank_mask(a, t);
+  for (int r = 0; r < a.ep; ++r) {
+    const uint64_t b = __ballot((m >> r) & 1);
+    if (lane == 0) wave_cnt[w][r] = __popcll(b);
+  }
+  __syncthreads();
+  for (int r = tid; r < a.ep; r += kTile) {
+    int c = 0;
+    for (int q = 0; q < kTileWaves; ++q) c += wave_cnt[q][r];
+    a.tile_rank[size_t(tile) * a.ep + r] = c;
+  }
+  for (int e = tid; e < a.E; e += kTile) a.tile_expert[size_t(tile) * a.E + e] = hist[e];
+}
+
+// One workgroup: rank r's tile counts become exclusive bases (one thread per
+// rank walks the tiles in order), expert e's counts are summed.
+__global__ __launch_bounds__(1024) void dl_scan_kernel(DlArgs a, int32_t* per_rank,
+                                                      int32_t* per_expert) {
+  const int tid = threadIdx.x;
+  if (tid < a.ep) {
+    int run = 0;
+    for (int j = 0; j < a.tiles; ++j) {
+      int32_t* p = a.tile_rank + size_t(j) * a.ep + tid;
+      const int c = *p;
+      *p = run;
+      run += c;
+    }
+    per_rank[tid] = run;
+  }
+  for (int e = tid; e < a.E; e += 1024) {
+    int s = 0;
+    for (int j = 0; j < a.tiles; ++j) s += a.tile_expert[size_t(j) * a.E + e];
+    per_expert[e] = s;
+  }
+}
+
+__global__ __launch_bounds__(kTile) void dl_place_kernel(DlArgs a, uint8_t* in_rank,
+                                                       int32_t* pos) {
+  __shared__ int32_t wave_cnt[kTileWaves][64];
+  const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
+  const int tile = blockIdx.x;
+  const int64_t t = int64_t(tile) * kTile + tid;
+  const uint64_t m = rank_mask(a, t);
+  const uint64_t below = lane == 0 ? 0ull : (~0ull >> (kWave - lane));
+  for (int r = 0; r < a.ep; ++r) {
+    const uint64_t b = __ballot((m >> r) & 1);
+    if (lane == 0) wave_cnt[w][r] = __popcll(b);
+  }
+  __syncthreads();
+  for (int r = 0; r < a.ep; ++r) {
+    // every lane takes part in the ballot; only tokens < T write
+    const uint64_t b = __ballot((m >> r) & 1);
+    const bool sent = (m >> r) & 1;
+    int before = a.tile_rank[size_t(tile) * a.ep + r] + __popcll(b & below);
+    for (int q = 0; q < w; ++q) before += wave_cnt[q][r];
+    if (t < a.T) {
+      in_rank[t * a.ep + r] = sent ? 1 : 0;
+      pos[t * a.ep + r] = sent ? before : -1;
+    }
+  }
+}
+
+}  // namespace
+
+size_t dispatch_layout_workspace_bytes(int64_t T, int E, int ep) {
+  const int64_t tiles = (T + kTile - 1) / kTile;
+  return size_t(tiles) * size_t(ep + E) * sizeof(int32_t);
+}
+
+hipError_t launch_dispatch_layout(const int32_t* idx, int64_t T, int E, int k, int ep,
+                                  int32_t* per_rank, int32_t* per_expert, uint8_t* in_rank,
+                                  int32_t* pos, void* ws, hipStream_t s) {
+  DlArgs a{};
+  a.idx = idx, a.T = T, a.E = E, a.k = k, a.ep = ep, a.el = E / ep;
+  a.tiles = static_cast<int>((T + kTile - 1) / kTile);
+  a.tile_rank = static_cast<int32_t*>(ws);
+  a.tile_expert = a.tile_rank + size_t(a.tiles) * ep;
+  if (a.tiles > 0) dl_count_kernel<<<a.tiles, kTile, 0, s>>>(a);
+  dl_scan_kernel<<<1, 1024, 0, s>>>(a, per_rank, per_expert);
+  if (a.tiles > 0) dl_place_kernel<<<a.tiles, kTile, 0, s>>>(a, in_rank, pos);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -121,6 +121,34 @@ int32_t moe_layout(const moe_layout_desc* desc, const int32_t* topk_idx_d,
                                       as_stream(stream)));
 }
 
+static bool dl_args_ok(int64_t T, int32_t E, int32_t k, int32_t ep) {
+  return T >= 0 && T < (int64_t(1) << 31) / 64 && E >= 1 && E <= kMaxExperts && k >= 1 &&
+         k <= std::min(E, kMaxTopK) && ep >= 1 && ep <= 64 && E % ep == 0;
+}
+
+size_t moe_dispatch_layout_workspace_bytes(int64_t num_tokens, int32_t num_experts,
+                                           int32_t top_k, int32_t ep_size) {
+  if (!dl_args_ok(num_tokens, num_experts, top_k, ep_size)) return 0;
+  return moe::dispatch_layout_workspace_bytes(num_tokens, num_experts, ep_size);
+}
+
+int32_t moe_dispatch_layout(const int32_t* topk_idx_d, int64_t num_tokens, int32_t num_experts,
+                            int32_t top_k, int32_t ep_size, int32_t* num_tokens_per_rank_d,
+                            int32_t* num_tokens_per_expert_d, uint8_t* is_token_in_rank_d,
+                            int32_t* token_rank_pos_d, void* workspace_d, size_t workspace_bytes,
+                            void* stream) {
+  if (!dl_args_ok(num_tokens, num_experts, top_k, ep_size)) return MOE_ERR_ARG;
+  if (!num_tokens_per_rank_d || !num_tokens_per_expert_d) return MOE_ERR_ARG;
+  const size_t need = moe::dispatch_layout_workspace_bytes(num_tokens, num_experts, ep_size);
+  if (num_tokens > 0 && (!topk_idx_d || !is_token_in_rank_d || !token_rank_pos_d ||
+                         !workspace_d || workspace_bytes < need))
+    return MOE_ERR_ARG;
+  return status_of(moe::launch_dispatch_layout(topk_idx_d, num_tokens, num_experts, top_k, ep_size,
+                                               num_tokens_per_rank_d, num_tokens_per_expert_d,
+                                               is_token_in_rank_d, token_rank_pos_d, workspace_d,
+                                               as_stream(stream)));
+}
+
 int32_t moe_permute(const void* x_d, int64_t num_tokens, int32_t hidden, int32_t top_k,
                     const int32_t* dst_row_d, int64_t m_cap, void* x_perm_d, void* stream) {
   if (num_tokens < 0 || hidden < 8 || hidden > kMaxHidden || hidden % 8 || top_k < 1 ||

@@ -149,6 +149,10 @@ hipError_t launch_gate_up_wgrad(const void* x_perm, const void* dgu, const int32
 hipError_t launch_down_wgrad(const void* h, const void* dy, const int32_t* offsets,
                              const int32_t* counts, int e_loc, int I, int H, void* dw2,
                              hipStream_t s);
+size_t dispatch_layout_workspace_bytes(int64_t T, int E, int ep);
+hipError_t launch_dispatch_layout(const int32_t* idx, int64_t T, int E, int k, int ep,
+                                  int32_t* per_rank, int32_t* per_expert, uint8_t* in_rank,
+                                  int32_t* pos, void* ws, hipStream_t s);
 
 int device_cu_count();
 

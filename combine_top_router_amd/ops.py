@@ -366,3 +366,25 @@ def grouped_down_wgrad(h, dy, offsets, counts, dw2=None):
         _ptr(h), _ptr(dy), _ptr(offsets), _ptr(counts), e_loc, m_cap, I, H, _ptr(dw2),
         _stream(h.device)))
     return dw2
+
+
+# ---------------------------------------------------------------- dedup layout
+
+def dispatch_layout(topk_idx: torch.Tensor, num_experts: int, ep_size: int):
+    """DeepEP-style per-rank layout: (num_tokens_per_rank [ep], num_tokens_per_expert [E],
+    is_token_in_rank [T, ep] uint8, token_rank_pos [T, ep] int32)."""
+    _need(topk_idx, "topk_idx", torch.int32)
+    T, k = topk_idx.shape
+    dev = topk_idx.device
+    ws_bytes = int(lib().moe_dispatch_layout_workspace_bytes(T, num_experts, k, ep_size))
+    if ws_bytes == 0 and T > 0:
+        raise MoEError("moe_dispatch_layout_workspace_bytes", 1, "invalid sizes")
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    per_rank = _empty((ep_size,), torch.int32, dev)
+    per_expert = _empty((num_experts,), torch.int32, dev)
+    in_rank = _empty((T, ep_size), torch.uint8, dev)
+    pos = _empty((T, ep_size), torch.int32, dev)
+    check("moe_dispatch_layout", lib().moe_dispatch_layout(
+        _ptr(topk_idx), T, num_experts, k, ep_size, _ptr(per_rank), _ptr(per_expert),
+        _ptr(in_rank), _ptr(pos), _ptr(ws), ws.numel(), _stream(dev)))
+    return per_rank, per_expert, in_rank, pos

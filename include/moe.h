@@ -136,6 +136,35 @@ int32_t moe_layout(const moe_layout_desc* desc, const int32_t* topk_idx_d,
                    size_t workspace_bytes, void* stream);
 
 /*
+ * moe_dispatch_layout -- per-rank deduplicated dispatch layout.
+ *
+ * The counts and table DeepEP's dispatch consumes, computed from topk_idx
+ * and the expert count before any data moves (DeepEP issue #272, the
+ * maintainer's example: get_dispatch_layout returns num_tokens_per_rank,
+ * num_tokens_per_expert and is_token_in_rank). A token is sent once to each
+ * rank that holds at least one of its experts (rank r holds experts
+ * [r*E/ep, (r+1)*E/ep)), however many of its slots land there:
+ *   is_token_in_rank_d      [T, ep] uint8: 1 if some slot of t maps to rank r
+ *   num_tokens_per_rank_d   [ep] int32: column sums of is_token_in_rank
+ *   num_tokens_per_expert_d [E] int32: assignments per expert
+ *   token_rank_pos_d        [T, ep] int32: position of t among the tokens rank r
+ *                           receives, in token order; -1 where t is not sent to r
+ * Expert ids outside [0, E) are skipped. No host sync; the result does not
+ * depend on scheduling.
+ *   workspace_d >= moe_dispatch_layout_workspace_bytes(...) bytes.
+ * Limits: 1 <= ep <= 64, E a multiple of ep, E <= 1024, 1 <= k <= min(E, 16),
+ * T < 2^25.
+ */
+size_t moe_dispatch_layout_workspace_bytes(int64_t num_tokens, int32_t num_experts,
+                                           int32_t top_k, int32_t ep_size);
+
+int32_t moe_dispatch_layout(const int32_t* topk_idx_d, int64_t num_tokens, int32_t num_experts,
+                            int32_t top_k, int32_t ep_size, int32_t* num_tokens_per_rank_d,
+                            int32_t* num_tokens_per_expert_d, uint8_t* is_token_in_rank_d,
+                            int32_t* token_rank_pos_d, void* workspace_d,
+                            size_t workspace_bytes, void* stream);
+
+/*
  * moe_permute -- expert-major token gather (the local part of dispatch).
  *
  * The reorder-by-expert step of the AutoEP flow (DeepSpeed AutoEP commit

@@ -92,3 +92,41 @@ def restore_default(y, dst_row, topk_w) -> np.ndarray:
         prod = bf16.round_to_bf16(w[m, s][:, None] * y[r[m]])
         out[m] = bf16.round_to_bf16(out[m] + prod)
     return out
+
+
+def combine_rows(y, dst_row, topk_w=None, shared=None, row_dtype: str = "bf16") -> np.ndarray:
+    """The fused restore for other row dtypes and the variants the pages name,
+    as float64 values of the returned rows.
+
+    * Row dtype (DeepSpeed PR #8847, section "Tests": the fused restore runs on
+      fp32 and on bf16 rows; section "Problem" and the fp16 note of the end-to-
+      end test: in fp16 the default restore rounds each product and addition).
+      Reading: the same FP32 slot-order sum as ``combine``, rounded once to the
+      row dtype -- bf16 or fp16 nearest even, none for fp32 rows.
+    * ``topk_w=None``: unit weights, the plain sum of a token's local rows
+      (the routing score was applied before the experts, AutoEP's
+      score_apply="pre" (same page, section "Change"), or the permute's
+      backward).
+    * ``shared``: rows [T, H] of a shared expert merged into the output (the
+      last step of the AutoEP runtime, DeepSpeed AutoEP commit text, section
+      "Design": merge shared experts if the model has them). Reading: added
+      in fp32 after the routed sum, before the one rounding."""
+    y32 = np.asarray(y).astype(np.float32)
+    dst = np.asarray(dst_row, dtype=np.int64)
+    T, k = dst.shape
+    w32 = (np.ones((T, k), dtype=np.float32) if topk_w is None
+           else np.asarray(topk_w).astype(np.float32))
+    out = np.zeros((T, y32.shape[1]), dtype=np.float32)
+    for s in range(k):
+        r = dst[:, s]
+        m = r >= 0
+        out[m] = out[m] + w32[m, s][:, None] * y32[r[m]]
+    if shared is not None:
+        out = out + np.asarray(shared).astype(np.float32)
+    if row_dtype == "fp32":
+        return out.astype(np.float64)
+    if row_dtype == "fp16":
+        return out.astype(np.float16).astype(np.float64)
+    if row_dtype == "bf16":
+        return bf16.round_to_bf16(out.astype(np.float64))
+    raise ValueError(f"unknown row dtype {row_dtype!r}")

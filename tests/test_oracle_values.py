@@ -190,3 +190,58 @@ def test_layer_equals_per_token_definition(share):
     np.testing.assert_allclose(res["out"], tok, rtol=1e-12, atol=1e-12)
     checks.check_layout(res["topk_idx"], res["layout"], cfg.num_experts, cfg.ep_size,
                         share, cfg.align)
+
+
+# ---------------------------------------------------------------- combine variants
+
+def test_combine_rows_fp32_is_the_fp32_sum():
+    rng = np.random.default_rng(4)
+    y = rng.standard_normal((10, 6))
+    dst = np.array([[0, 3], [1, -1], [2, 9], [-1, -1], [4, 5]])
+    w = rng.random((5, 2))
+    np.testing.assert_array_equal(ocombine.combine_rows(y, dst, w, row_dtype="fp32"),
+                                  ocombine.combine(y, dst, w).astype(np.float64))
+
+
+def test_combine_rows_rounds_once_to_the_row_dtype():
+    # fp16: 1 + 2^-11 is a tie between 1 and 1 + 2^-10 -> 1 (even); bf16: 1 + 2^-8 -> 1
+    y = np.array([[1.0], [2.0 ** -11], [2.0 ** -8]])
+    dst = np.array([[0, 1]])
+    assert ocombine.combine_rows(y, dst, row_dtype="fp16")[0, 0] == 1.0
+    dst2 = np.array([[0, 2]])
+    assert ocombine.combine_rows(y, dst2, row_dtype="bf16")[0, 0] == 1.0
+    # just above the fp16 tie rounds up
+    y3 = np.array([[1.0], [2.0 ** -11 + 2.0 ** -20]])
+    assert ocombine.combine_rows(y3, np.array([[0, 1]]), row_dtype="fp16")[0, 0] == 1.0 + 2.0 ** -10
+
+
+def test_shared_rows_join_before_the_one_rounding():
+    # routed sum 1 + 3*2^-9 and shared rows -2^-9: the fp32 sum 1 + 2^-8 is a
+    # bf16 tie that rounds to even, 1.0; rounding the routed part first would
+    # give 1 + 2^-7 and keep it
+    y = np.array([[1.0 + 3 * 2.0 ** -9]])
+    dst = np.array([[0]])
+    shared = np.array([[-2.0 ** -9]])
+    assert ocombine.combine_rows(y, dst, shared=shared)[0, 0] == 1.0
+    routed_first = bf16.round_to_bf16(bf16.round_to_bf16(1.0 + 3 * 2.0 ** -9) - 2.0 ** -9)
+    assert routed_first == 1.0 + 2.0 ** -7
+
+
+def test_score_before_and_after_the_experts_agree_for_identity_experts():
+    # with identity experts, applying the score before (permute_weighted, then a
+    # unit-weight combine) and after (the weighted combine) give the same
+    # sum up to the roundings each path makes
+    rng = np.random.default_rng(9)
+    T, k, E, H = 12, 2, 4, 8
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    idx = oroute.select(logits, k)
+    w = oroute.weights(logits, idx)
+    L = olayout.layout(idx, E, 1, -1, 4)
+    x = bf16.round_to_bf16(rng.standard_normal((T, H)))
+    rows = int(L["offsets"][-1])
+    xp_pre, _ = opermute.permute_weighted(x, L["dst_row"], w, rows)
+    pre = ocombine.combine_rows(xp_pre, L["dst_row"], None)
+    post = ocombine.combine_rows(opermute.permute(x, L["src_row"], k), L["dst_row"], w)
+    exact = ocombine.combine_exact(opermute.permute(x, L["src_row"], k), L["dst_row"], w)
+    assert np.abs(pre - exact).max() <= 2.0 ** -6 * np.abs(exact).max()
+    assert np.abs(post - exact).max() <= 2.0 ** -7 * np.abs(exact).max()

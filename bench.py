@@ -145,7 +145,7 @@ def cpu_baseline(cfg, dist, layer_args, budget_s):
                        f"{len(os.sched_getaffinity(0))} host cores visible")}
 
 
-def time_backward(args, cfg, layer, moe, stream, t_loc, n_loc, weights):
+def time_backward(args, cfg, layer, moe, stream, t_loc, n_loc, weights, x):
     """Per-call times of the calls outside the step, on this step's routing
     and rows, after the forward timing (not part of ``value``): the forward
     gate/up that also keeps the pre-activations, then the backward chain
@@ -175,6 +175,7 @@ def time_backward(args, cfg, layer, moe, stream, t_loc, n_loc, weights):
     dw2 = torch.empty((e_loc, I, H), dtype=torch.bfloat16, device=dev)
     dst, off, cnt = L.dst_row, L.offsets, L.local_counts
     dl_ep = max(cfg.ep_size, 8) if E % max(cfg.ep_size, 8) == 0 else cfg.ep_size
+    sh = workloads.gen.random_rows(cfg, T, torch.bfloat16, args.seed, device=dev)
     nhi = float(n_loc) * H * I
     calls = [
         ("gate_up_save", lambda: moe.ops.grouped_gate_up_save(
@@ -193,6 +194,13 @@ def time_backward(args, cfg, layer, moe, stream, t_loc, n_loc, weights):
          "mfma", 4 * nhi),
         ("permute_backward", lambda: moe.ops.permute_backward(dxp, dst, gx),
          "hbm", n_loc * H * 2 + T * H * 2 + T * k * 4),
+        # restore variants: the shared expert's rows merged, and the permute
+        # that applies the score before the experts
+        ("combine_shared", lambda: moe.ops.combine_rows(layer.y, dst, layer.topk_w, sh, gx),
+         "hbm", n_loc * H * 2 + T * k * 8 + 2 * T * H * 2),
+        ("permute_weighted", lambda: moe.ops.permute_weighted(x, dst, layer.topk_w,
+                                                              layer.m_cap, dxp),
+         "hbm", (t_loc + n_loc) * H * 2 + T * k * 8),
         # the per-rank deduplicated layout (over the workload's ep virtual
         # ranks, at least 8): T*k ids read, the [T, ep] table and positions written
         ("dispatch_layout", lambda: moe.ops.dispatch_layout(layer.topk_idx, E, dl_ep),
@@ -325,7 +333,7 @@ def main():
                 "unit": "GB/s", "frac": d["frac"], "traffic": traffic}
 
     backward = None if args.no_backward else time_backward(args, cfg, layer, moe, stream,
-                                                            t_loc, n_loc, (w1, w3, w2))
+                                                            t_loc, n_loc, (w1, w3, w2), x)
 
     cpu = None
     if not args.no_cpu_baseline:

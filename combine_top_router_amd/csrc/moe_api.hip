@@ -157,7 +157,20 @@ int32_t moe_permute(const void* x_d, int64_t num_tokens, int32_t hidden, int32_t
   if (num_tokens == 0) return MOE_OK;
   if (!x_d || !dst_row_d || !x_perm_d || !aligned16(x_d) || !aligned16(x_perm_d))
     return MOE_ERR_ARG;
-  return status_of(moe::launch_permute(x_d, num_tokens, hidden, top_k, dst_row_d, m_cap,
+  return status_of(moe::launch_permute(x_d, num_tokens, hidden, top_k, dst_row_d, nullptr, m_cap,
+                                       x_perm_d, as_stream(stream)));
+}
+
+int32_t moe_permute_weighted(const void* x_d, int64_t num_tokens, int32_t hidden, int32_t top_k,
+                             const int32_t* dst_row_d, const float* topk_w_d, int64_t m_cap,
+                             void* x_perm_d, void* stream) {
+  if (num_tokens < 0 || hidden < 8 || hidden > kMaxHidden || hidden % 8 || top_k < 1 ||
+      top_k > kMaxTopK || m_cap < 0)
+    return MOE_ERR_ARG;
+  if (num_tokens == 0) return MOE_OK;
+  if (!x_d || !dst_row_d || !topk_w_d || !x_perm_d || !aligned16(x_d) || !aligned16(x_perm_d))
+    return MOE_ERR_ARG;
+  return status_of(moe::launch_permute(x_d, num_tokens, hidden, top_k, dst_row_d, topk_w_d, m_cap,
                                        x_perm_d, as_stream(stream)));
 }
 
@@ -333,6 +346,23 @@ int32_t moe_route_backward(const int32_t* topk_idx_d, const float* topk_w_d,
   return status_of(moe::launch_route_backward(topk_idx_d, topk_w_d, grad_w_d, num_tokens,
                                               num_experts, top_k, grad_logits_d,
                                               as_stream(stream)));
+}
+
+int32_t moe_combine_rows(const void* y_d, int32_t row_dtype, int64_t y_rows,
+                         const int32_t* dst_row_d, const float* topk_w_d, const void* shared_d,
+                         int64_t num_tokens, int32_t hidden, int32_t top_k, void* out_d,
+                         void* stream) {
+  if (num_tokens < 0 || y_rows < 0 || hidden < 8 || hidden > kMaxHidden || hidden % 8 ||
+      top_k < 1 || top_k > kMaxTopK)
+    return MOE_ERR_ARG;
+  if (row_dtype != MOE_ROWS_BF16 && row_dtype != MOE_ROWS_F16 && row_dtype != MOE_ROWS_F32)
+    return MOE_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return MOE_OK;
+  if (!dst_row_d || !out_d || !aligned16(out_d)) return MOE_ERR_ARG;
+  if (y_rows > 0 && (!y_d || !aligned16(y_d))) return MOE_ERR_ARG;
+  if (shared_d && !aligned16(shared_d)) return MOE_ERR_ARG;
+  return status_of(moe::launch_combine_rows(y_d, row_dtype, y_rows, dst_row_d, topk_w_d, shared_d,
+                                            num_tokens, hidden, top_k, out_d, as_stream(stream)));
 }
 
 int32_t moe_validate_layout(const moe_layout_desc* desc, const int32_t* topk_idx_d,

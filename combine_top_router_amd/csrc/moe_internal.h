@@ -118,9 +118,13 @@ hipError_t launch_layout(const LayoutPlan& p, const int32_t* topk_idx, int32_t* 
                          int32_t* src_row, int64_t m_cap, void* ws, hipStream_t s);
 
 hipError_t launch_permute(const void* x, int64_t T, int H, int k, const int32_t* dst_row,
-                          int64_t m_cap, void* x_perm, hipStream_t s);
+                          const float* topk_w, int64_t m_cap, void* x_perm, hipStream_t s);
 hipError_t launch_combine(const void* y, int64_t y_rows, const int32_t* dst_row, const float* w,
                           int64_t T, int H, int k, void* out, hipStream_t s);
+// row_type: 0 bf16, 1 fp16, 2 fp32; w and shared may be null
+hipError_t launch_combine_rows(const void* y, int row_type, int64_t y_rows,
+                               const int32_t* dst_row, const float* w, const void* shared,
+                               int64_t T, int H, int k, void* out, hipStream_t s);
 hipError_t launch_combine_backward(const void* grad_out, const void* y, int64_t y_rows,
                                    const int32_t* dst_row, const float* w, int64_t T, int H,
                                    int k, void* grad_y, float* grad_w, hipStream_t s);

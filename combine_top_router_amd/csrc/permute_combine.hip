@@ -25,11 +25,15 @@ constexpr int kTokensPerBlock = 4;  // one wavefront each
 // Each lane buffers up to kBuf vectors of its token's row before storing.
 constexpr int kBuf = 16;  // 16 x 64 lanes x 8 bf16 = 8192 elements per pass
 
-template <int K>
+// With weights (the score applied before the experts) each copy is
+// bf16(w[t, s] * x[t]), an fp32 product rounded once.
+template <int K, bool WEIGHTED>
 __global__ __launch_bounds__(256) void permute_kernel(const u32x4* __restrict__ x, int64_t T,
                                                       int hv, int k_rt,
                                                       const int32_t* __restrict__ dst_row,
+                                                      const float* __restrict__ topk_w,
                                                       int64_t m_cap, u32x4* __restrict__ x_perm) {
+#pragma clang fp contract(off)
   const int k = K > 0 ? K : k_rt;
   const int64_t t = uniform(static_cast<int64_t>(blockIdx.x) * kTokensPerBlock +
                             threadIdx.x / kWave);
@@ -62,24 +66,88 @@ __global__ __launch_bounds__(256) void permute_kernel(const u32x4* __restrict__ 
     for (int j = 0; j < (K > 0 ? K : 16); ++j) {
       if (j >= k || rows[j] < 0) continue;
       u32x4* dst = x_perm + rows[j] * hv;
+      if constexpr (WEIGHTED) {
+        const float w = topk_w[t * k + j];
 #pragma unroll
-      for (int i = 0; i < kBuf; ++i) {
-        const int v = base + i * kWave + lane;
-        if (v < hv) dst[v] = buf[i];
+        for (int i = 0; i < kBuf; ++i) {
+          const int v = base + i * kWave + lane;
+          if (v < hv) {
+            float f[8];
+            unpack8(buf[i], f);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) f[q] = w * f[q];
+            dst[v] = pack8(f);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < kBuf; ++i) {
+          const int v = base + i * kWave + lane;
+          if (v < hv) dst[v] = buf[i];
+        }
       }
     }
   }
 }
 
-template <int K>
+// Row element types of the combine: bf16 (8 per 16-byte vector), fp16 (8),
+// fp32 (4).
+enum RowType { kRowBf16 = 0, kRowF16 = 1, kRowF32 = 2 };
+
+template <int RT>
+struct Rows {
+  static constexpr int NV = RT == kRowF32 ? 4 : 8;  // elements per 16-byte vector
+  __device__ static void load(const u32x4& v, float (&f)[NV]) {
+    if constexpr (RT == kRowBf16) {
+      unpack8(v, f);
+    } else if constexpr (RT == kRowF16) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t word = v[i];
+        f[2 * i] = static_cast<float>(__builtin_bit_cast(_Float16, uint16_t(word & 0xffffu)));
+        f[2 * i + 1] = static_cast<float>(__builtin_bit_cast(_Float16, uint16_t(word >> 16)));
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) f[i] = __uint_as_float(v[i]);
+    }
+  }
+  __device__ static u32x4 store(const float (&f)[NV]) {
+    if constexpr (RT == kRowBf16) {
+      return pack8(f);
+    } else if constexpr (RT == kRowF16) {
+      u32x4 v;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t lo = __builtin_bit_cast(uint16_t, static_cast<_Float16>(f[2 * i]));  // nearest even
+        const uint32_t hi = __builtin_bit_cast(uint16_t, static_cast<_Float16>(f[2 * i + 1]));
+        v[i] = lo | (hi << 16);
+      }
+      return v;
+    } else {
+      u32x4 v;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = __float_as_uint(f[i]);
+      return v;
+    }
+  }
+};
+
+// out[t] = round( sum over local slots, in slot order, of w[t, s] * y[r]
+//                 (+ shared[t]) ), fp32 products and sums, one rounding to the
+// row type. No weight array: every weight is 1. No shared rows: nothing added.
+template <int K, int RT>
 __global__ __launch_bounds__(256) void combine_kernel(const u32x4* __restrict__ y, int64_t y_rows,
                                                       const int32_t* __restrict__ dst_row,
                                                       const float* __restrict__ topk_w,
+                                                      const u32x4* __restrict__ shared,
                                                       int64_t T, int hv, int k_rt,
                                                       u32x4* __restrict__ out) {
   // fp32 product, then fp32 sum: two IEEE roundings per slot, never contracted
   // to an FMA, so the result is the plain fp32 slot-order sum
 #pragma clang fp contract(off)
+  using R = Rows<RT>;
+  constexpr int NV = R::NV;
   const int k = K > 0 ? K : k_rt;
   constexpr int KM = K > 0 ? K : 16;
   const int64_t t = uniform(static_cast<int64_t>(blockIdx.x) * kTokensPerBlock +
@@ -94,7 +162,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const u32x4* __restrict__ 
     if (j < k) {
       const int r = dst_row[t * k + j];
       rows[j] = (r >= 0 && r < y_rows) ? int64_t(r) : -1;
-      w[j] = topk_w ? topk_w[t * k + j] : 1.0f;  // no weights: the permute's backward
+      w[j] = topk_w ? topk_w[t * k + j] : 1.0f;  // no weights: a plain sum
     } else {
       rows[j] = -1;
       w[j] = 0.f;
@@ -107,55 +175,84 @@ __global__ __launch_bounds__(256) void combine_kernel(const u32x4* __restrict__ 
 #pragma unroll
     for (int j = 0; j < KM; ++j)
       if (rows[j] >= 0) in[j] = __builtin_nontemporal_load(y + rows[j] * hv + v);
-    float acc[8];
+    float acc[NV];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) acc[q] = 0.f;
+    for (int q = 0; q < NV; ++q) acc[q] = 0.f;
 #pragma unroll
     for (int j = 0; j < KM; ++j) {
       if (rows[j] < 0) continue;
-      float f[8];
-      unpack8(in[j], f);
+      float f[NV];
+      R::load(in[j], f);
 #pragma unroll
-      for (int q = 0; q < 8; ++q) acc[q] = acc[q] + w[j] * f[q];
+      for (int q = 0; q < NV; ++q) acc[q] = acc[q] + w[j] * f[q];
     }
-    __builtin_nontemporal_store(pack8(acc), dst + v);
+    if (shared) {  // the shared expert's row joins before the one rounding
+      float f[NV];
+      R::load(__builtin_nontemporal_load(shared + t * hv + v), f);
+#pragma unroll
+      for (int q = 0; q < NV; ++q) acc[q] = acc[q] + f[q];
+    }
+    __builtin_nontemporal_store(R::store(acc), dst + v);
   }
 }
 
 }  // namespace
 
 hipError_t launch_permute(const void* x, int64_t T, int H, int k, const int32_t* dst_row,
-                          int64_t m_cap, void* x_perm, hipStream_t s) {
+                          const float* topk_w, int64_t m_cap, void* x_perm, hipStream_t s) {
   if (T == 0) return hipSuccess;
   const int hv = H / 8;
   const dim3 grid(static_cast<unsigned>((T + kTokensPerBlock - 1) / kTokensPerBlock));
   const u32x4* xs = static_cast<const u32x4*>(x);
   u32x4* xp = static_cast<u32x4*>(x_perm);
+#define MOE_PERMUTE(KK)                                                                          \
+  (topk_w ? permute_kernel<KK, true><<<grid, 256, 0, s>>>(xs, T, hv, k, dst_row, topk_w, m_cap, xp) \
+          : permute_kernel<KK, false><<<grid, 256, 0, s>>>(xs, T, hv, k, dst_row, topk_w, m_cap, xp))
   switch (k) {
-    case 1: permute_kernel<1><<<grid, 256, 0, s>>>(xs, T, hv, k, dst_row, m_cap, xp); break;
-    case 2: permute_kernel<2><<<grid, 256, 0, s>>>(xs, T, hv, k, dst_row, m_cap, xp); break;
-    case 4: permute_kernel<4><<<grid, 256, 0, s>>>(xs, T, hv, k, dst_row, m_cap, xp); break;
-    case 6: permute_kernel<6><<<grid, 256, 0, s>>>(xs, T, hv, k, dst_row, m_cap, xp); break;
-    case 8: permute_kernel<8><<<grid, 256, 0, s>>>(xs, T, hv, k, dst_row, m_cap, xp); break;
-    default: permute_kernel<0><<<grid, 256, 0, s>>>(xs, T, hv, k, dst_row, m_cap, xp); break;
+    case 1: MOE_PERMUTE(1); break;
+    case 2: MOE_PERMUTE(2); break;
+    case 4: MOE_PERMUTE(4); break;
+    case 6: MOE_PERMUTE(6); break;
+    case 8: MOE_PERMUTE(8); break;
+    default: MOE_PERMUTE(0); break;
   }
+#undef MOE_PERMUTE
   return hipGetLastError();
+}
+
+template <int RT>
+static void combine_for(const void* y, int64_t y_rows, const int32_t* dst_row, const float* w,
+                        const void* shared, int64_t T, int H, int k, void* out, hipStream_t s) {
+  const int hv = H / Rows<RT>::NV;
+  const dim3 grid(static_cast<unsigned>((T + kTokensPerBlock - 1) / kTokensPerBlock));
+  const u32x4* ys = static_cast<const u32x4*>(y);
+  const u32x4* sh = static_cast<const u32x4*>(shared);
+  u32x4* o = static_cast<u32x4*>(out);
+#define MOE_COMBINE(KK) combine_kernel<KK, RT><<<grid, 256, 0, s>>>(ys, y_rows, dst_row, w, sh, T, hv, k, o)
+  switch (k) {
+    case 1: MOE_COMBINE(1); break;
+    case 2: MOE_COMBINE(2); break;
+    case 4: MOE_COMBINE(4); break;
+    case 6: MOE_COMBINE(6); break;
+    case 8: MOE_COMBINE(8); break;
+    default: MOE_COMBINE(0); break;
+  }
+#undef MOE_COMBINE
 }
 
 hipError_t launch_combine(const void* y, int64_t y_rows, const int32_t* dst_row, const float* w,
                           int64_t T, int H, int k, void* out, hipStream_t s) {
+  return launch_combine_rows(y, 0, y_rows, dst_row, w, nullptr, T, H, k, out, s);
+}
+
+hipError_t launch_combine_rows(const void* y, int row_type, int64_t y_rows,
+                               const int32_t* dst_row, const float* w, const void* shared,
+                               int64_t T, int H, int k, void* out, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  const int hv = H / 8;
-  const dim3 grid(static_cast<unsigned>((T + kTokensPerBlock - 1) / kTokensPerBlock));
-  const u32x4* ys = static_cast<const u32x4*>(y);
-  u32x4* o = static_cast<u32x4*>(out);
-  switch (k) {
-    case 1: combine_kernel<1><<<grid, 256, 0, s>>>(ys, y_rows, dst_row, w, T, hv, k, o); break;
-    case 2: combine_kernel<2><<<grid, 256, 0, s>>>(ys, y_rows, dst_row, w, T, hv, k, o); break;
-    case 4: combine_kernel<4><<<grid, 256, 0, s>>>(ys, y_rows, dst_row, w, T, hv, k, o); break;
-    case 6: combine_kernel<6><<<grid, 256, 0, s>>>(ys, y_rows, dst_row, w, T, hv, k, o); break;
-    case 8: combine_kernel<8><<<grid, 256, 0, s>>>(ys, y_rows, dst_row, w, T, hv, k, o); break;
-    default: combine_kernel<0><<<grid, 256, 0, s>>>(ys, y_rows, dst_row, w, T, hv, k, o); break;
+  switch (row_type) {
+    case kRowBf16: combine_for<kRowBf16>(y, y_rows, dst_row, w, shared, T, H, k, out, s); break;
+    case kRowF16: combine_for<kRowF16>(y, y_rows, dst_row, w, shared, T, H, k, out, s); break;
+    default: combine_for<kRowF32>(y, y_rows, dst_row, w, shared, T, H, k, out, s); break;
   }
   return hipGetLastError();
 }

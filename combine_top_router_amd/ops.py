@@ -388,3 +388,47 @@ def dispatch_layout(topk_idx: torch.Tensor, num_experts: int, ep_size: int):
         _ptr(topk_idx), T, num_experts, k, ep_size, _ptr(per_rank), _ptr(per_expert),
         _ptr(in_rank), _ptr(pos), _ptr(ws), ws.numel(), _stream(dev)))
     return per_rank, per_expert, in_rank, pos
+
+
+# ---------------------------------------------------------------- variants
+
+_ROWS = {torch.bfloat16: 0, torch.float16: 1, torch.float32: 2}
+
+
+def permute_weighted(x: torch.Tensor, dst_row: torch.Tensor, topk_w: torch.Tensor, m_cap: int,
+                     out=None) -> torch.Tensor:
+    """x_perm with the routing score applied before the experts:
+    row dst_row[t, s] = bf16(w[t, s] * x[t])."""
+    _need(x, "x", torch.bfloat16)
+    T, H = x.shape
+    _need(dst_row, "dst_row", torch.int32)
+    k = dst_row.shape[1]
+    _need(topk_w, "topk_w", torch.float32, (T, k))
+    out = _empty((m_cap, H), torch.bfloat16, x.device) if out is None else out
+    _need(out, "x_perm", torch.bfloat16, (m_cap, H))
+    check("moe_permute_weighted", lib().moe_permute_weighted(
+        _ptr(x), T, H, k, _ptr(dst_row), _ptr(topk_w), m_cap, _ptr(out), _stream(x.device)))
+    return out
+
+
+def combine_rows(y: torch.Tensor, dst_row: torch.Tensor, topk_w=None, shared=None, out=None):
+    """The fused restore on bf16 / fp16 / fp32 rows: fp32 slot-order sum of
+    w * y (w = 1 without weights), plus the shared expert's rows if given,
+    rounded once to the row dtype."""
+    if y.dtype not in _ROWS:
+        raise TypeError(f"y must be bf16, fp16 or fp32 (got {y.dtype})")
+    _need(y, "y", y.dtype)
+    _need(dst_row, "dst_row", torch.int32)
+    T, k = dst_row.shape
+    H = y.shape[1]
+    if topk_w is not None:
+        _need(topk_w, "topk_w", torch.float32, (T, k))
+    if shared is not None:
+        _need(shared, "shared", y.dtype, (T, H))
+    out = _empty((T, H), y.dtype, y.device) if out is None else out
+    _need(out, "out", y.dtype, (T, H))
+    check("moe_combine_rows", lib().moe_combine_rows(
+        _ptr(y), _ROWS[y.dtype], y.shape[0], _ptr(dst_row),
+        _ptr(topk_w) if topk_w is not None else None,
+        _ptr(shared) if shared is not None else None, T, H, k, _ptr(out), _stream(y.device)))
+    return out

@@ -183,6 +183,18 @@ int32_t moe_permute(const void* x_d, int64_t num_tokens, int32_t hidden, int32_t
                     void* stream);
 
 /*
+ * moe_permute_weighted -- the permute with the routing score applied before
+ * the experts (AutoEP's score_apply="pre", DeepSpeed PR #8847, section
+ * "Change", which the fused restore refuses): x_perm[dst_row[t, s], :] =
+ * bf16(topk_w[t, s] * x[t, :]), an fp32 product rounded once. The experts
+ * then see scaled rows and the restore is a plain sum (moe_combine_rows with
+ * no weights). Arguments and limits as moe_permute, plus topk_w_d [T, k].
+ */
+int32_t moe_permute_weighted(const void* x_d, int64_t num_tokens, int32_t hidden, int32_t top_k,
+                             const int32_t* dst_row_d, const float* topk_w_d, int64_t m_cap,
+                             void* x_perm_d, void* stream);
+
+/*
  * moe_pack_weights -- one-time repack of expert matrices to the layout the
  * grouped GEMM reads: wt[e, c, r] = w[e, r, c] for e < num_mats, a bit copy.
  * Expert weights arrive in math orientation (gate/up [E, H, I], down
@@ -371,6 +383,33 @@ int32_t moe_permute_backward(const void* grad_x_perm_d, int64_t x_perm_rows,
 int32_t moe_route_backward(const int32_t* topk_idx_d, const float* topk_w_d,
                            const float* grad_w_d, int64_t num_tokens, int32_t num_experts,
                            int32_t top_k, float* grad_logits_d, void* stream);
+
+/*
+ * moe_combine_rows -- the fused restore on other row dtypes and variants.
+ *
+ * The fused restore runs on bf16 and on fp32 rows (DeepSpeed PR #8847,
+ * section "Tests"); fp16 rows are the third activation dtype the page
+ * discusses. Per token t:
+ *
+ *   out[t, :] = round( sum over local slots s, in slot order, of w[t, s] * y[dst_row[t, s], :]
+ *                      + shared[t, :] )
+ *
+ * in fp32 (products, then sums, no fused multiply-add) and rounded once to the
+ * row dtype (nearest even; fp32 rows are not rounded again). topk_w_d = NULL
+ * gives w = 1, the plain sum used when the score was applied before the
+ * experts (moe_permute_weighted). shared_d = NULL adds nothing; otherwise it
+ * holds the output rows [T, H] of a shared expert, merged as the last step of
+ * the AutoEP runtime (DeepSpeed AutoEP commit text, section "Design": merge
+ * shared experts if the model has them). y_d, shared_d and out_d are all of
+ * the row dtype; MOE_ROWS_BF16 with weights and no shared rows is moe_combine.
+ * Limits as moe_combine.
+ */
+enum { MOE_ROWS_BF16 = 0, MOE_ROWS_F16 = 1, MOE_ROWS_F32 = 2 };
+
+int32_t moe_combine_rows(const void* y_d, int32_t row_dtype, int64_t y_rows,
+                         const int32_t* dst_row_d, const float* topk_w_d, const void* shared_d,
+                         int64_t num_tokens, int32_t hidden, int32_t top_k, void* out_d,
+                         void* stream);
 
 /*
  * moe_validate_layout -- debug check of a layout (SYNCHRONISES the stream,

@@ -125,3 +125,10 @@ def output_gradient(cfg: MoEConfig, seed: int = 0, device="cpu") -> torch.Tensor
 def score_gradient(cfg: MoEConfig, seed: int = 0, device="cpu") -> torch.Tensor:
     """Stand-in gradient of the routing weights [T, k] fp32, N(0, 1)."""
     return _randn((cfg.num_tokens, cfg.top_k), 1.0, device, cfg.name, "grad_w", seed)
+
+
+def random_rows(cfg: MoEConfig, rows: int, dtype: torch.dtype, seed: int = 0,
+                device="cpu") -> torch.Tensor:
+    """Rows [rows, H] of N(0, 1) values in ``dtype`` (fp32 rows keep all 24
+    bits), for exercising the row movers on their own."""
+    return _randn((rows, cfg.hidden), 1.0, device, cfg.name, "rows", str(dtype), seed).to(dtype)

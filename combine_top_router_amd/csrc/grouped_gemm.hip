@@ -40,8 +40,10 @@
 //    then n-tile, then m-tile, and each of the 8 XCDs gets a contiguous range
 //    of ids, so the workgroups sharing a weight tile or an activation tile
 //    sit behind the same L2. An expert's c rows form ceil(c/BM) tiles of
-//    equal height, so no tile is a short tail that would finish early and
-//    pull its workgroup out of step with the others sharing its data.
+//    (nearly) equal height, so no tile is a short tail that would finish
+//    early and pull its workgroup out of step with the others sharing its
+//    data. Each wavefront runs a K loop specialised for the number of its
+//    32-row blocks that hold rows.
 //  * Each tile's A range ends at its expert's last row: the rows past it
 //    read as zeros through the buffer bound (their results are never stored).
 //  * Epilogue through LDS: fp32 -> bf16 (SwiGLU for the gated pair) into a
@@ -105,6 +107,18 @@ __device__ __forceinline__ int swz_key(int row) {
 template <int BK>
 __device__ __forceinline__ int swz(int row, int ch) {
   return row * (BK * 2) + ((ch ^ swz_key<BK>(row)) << 4);
+}
+
+// Calls f(std::integral_constant<int, nb>) for the run-time nb in 0..NB, so
+// each block count gets its own fully unrolled copy of f.
+template <int NB, class F>
+__device__ __forceinline__ void with_block_count(int nb, F&& f) {
+  if constexpr (NB == 0) {
+    f(std::integral_constant<int, 0>{});
+  } else {
+    if (nb >= NB) f(std::integral_constant<int, NB>{});
+    else with_block_count<NB - 1>(nb, f);
+  }
 }
 
 template <int BM, int BN, int BK, int STAGES, int KIND, int TM>
@@ -194,13 +208,25 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
     const int mtiles = uniform(mt_prefix[e + 1] - mt_prefix[e]);
     const int rem = tile - uniform(mt_prefix[e]) * NT;
     const int nt = rem / mtiles, mt = rem % mtiles;
-    // the expert's rows split into mtiles tiles of equal height (a multiple
-    // of 32, at most BM): no short tail tile, so the workgroups that share
-    // weight and activation tiles through L2 take equally long and stay in step
+    // The expert's rows split into mtiles tiles of (nearly) equal height, a
+    // multiple of 32 and at most BM: no short tail tile, so the workgroups that
+    // share weight and activation tiles through L2 take about equally long and
+    // stay in step. The gated kinds deal the expert's 32-row blocks out evenly
+    // (heights differ by at most one block, nothing is computed past the last
+    // block); the others give every tile the same height, the last one
+    // holding what is left (measured faster for them).
     const int cnt_e = uniform(g.counts[e]);
-    const int hgt = ((cnt_e + mtiles - 1) / mtiles + 31) / 32 * 32;
-    const int64_t row0 = int64_t(uniform(g.offsets[e])) + int64_t(mt) * hgt;
-    const int rows_valid = min(hgt, cnt_e - mt * hgt);
+    int hgt, start;
+    if constexpr (GATED) {
+      const int blks = (cnt_e + 31) / 32, bq = blks / mtiles, br = blks % mtiles;
+      hgt = (bq + (mt < br ? 1 : 0)) * 32;
+      start = 32 * (mt * bq + min(mt, br));
+    } else {
+      hgt = ((cnt_e + mtiles - 1) / mtiles + 31) / 32 * 32;
+      start = mt * hgt;
+    }
+    const int64_t row0 = int64_t(uniform(g.offsets[e])) + start;
+    const int rows_valid = min(hgt, cnt_e - start);
 
     // scalar bases + 32-bit per-lane offsets (elements) within the tile
     const uint16_t* a_base = g.a + row0 * K;
@@ -314,13 +340,9 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
         mfma(fa[(KK - 1) & 1], fb[(KK - 1) & 1]);
       }
     };
-    // one K-loop copy per supported block count; a count without its own copy
-    // runs the next larger one (the extra blocks multiply rows that are never
-    // stored)
-    if (nblk > TM / 2 + 1 || nblk == TM) kloop(std::integral_constant<int, TM>{});
-    else if (TM > 2 && nblk > 1) kloop(std::integral_constant<int, TM / 2 + 1>{});
-    else if (nblk == 1) kloop(std::integral_constant<int, 1>{});
-    else kloop(std::integral_constant<int, 0>{});
+    // one K-loop copy per block count 0..TM: a wavefront multiplies only the
+    // blocks that hold rows
+    with_block_count<TM>(nblk, kloop);
     __syncthreads();  // every wavefront is done reading the last slice
 
     // accumulators (lane: column lane % 32, rows 8*(q/4) + 4*(lane/32) + q%4)

@@ -61,8 +61,9 @@ constexpr int kMaxExperts = 1024;
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * kWave;
 
-// What a launch computes (the B operand is always [E_loc, N, ldb], rows
-// K-contiguous):
+// What a launch computes. The B operand holds, per local expert, N output
+// rows of K: for the forward kinds (kPlain, kGated, kGatedSave) in the packed
+// layout of moe_pack_weights, for the backward kinds row-major [E_loc, N, ldb].
 //   kPlain      c = a b0^T                                  (down; any plain product)
 //   kGated      c = silu(a b0^T) * (a b1^T)                 (gate/up, SwiGLU fused)
 //   kGatedSave  as kGated, and aux_out = [a b0^T | a b1^T]  (pre-activations kept for
@@ -75,14 +76,14 @@ enum Kind { kPlain = 0, kGated = 1, kGatedSave = 2, kSwigluBwd = 3, kKSplit = 4 
 
 struct GemmArgs {
   const uint16_t* a;       // [rows, K] bf16
-  const uint16_t* b0;      // [E_loc, N, ldb] bf16
-  const uint16_t* b1;      // [E_loc, N, ldb] bf16 (kGated*, kKSplit)
+  const uint16_t* b0;      // [E_loc, N, K] bf16 packed, or [E_loc, N, ldb] row-major
+  const uint16_t* b1;      // as b0 (kGated*, kKSplit)
   uint16_t* c;             // [rows, N] bf16 ([rows, 2N] for kSwigluBwd)
   const int32_t* offsets;  // [E_loc + 1]
   const int32_t* counts;   // [E_loc]
   int e_loc;
   int n, k;
-  int ldb;                 // row length of b0/b1: K, or k_split for kKSplit
+  int ldb;                 // row-major b0/b1: row length (K, or k_split for kKSplit)
   int k_split;             // kKSplit: K index where b1 takes over
   const uint16_t* aux;     // kSwigluBwd: [rows, 2N] bf16, (g | u) of the forward
   uint16_t* aux_out;       // kGatedSave: [rows, 2N] bf16 (out)
@@ -124,6 +125,8 @@ __device__ __forceinline__ void with_block_count(int nb, F&& f) {
 template <int BM, int BN, int BK, int STAGES, int KIND, int TM>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
   constexpr bool GATED = KIND == kGated || KIND == kGatedSave;
+  // the forward kinds read packed weights, the backward kinds row-major ones
+  constexpr bool BLOCKED = KIND == kGated || KIND == kGatedSave || KIND == kPlain;
   constexpr int WROWS = 32 * TM;               // accumulator rows per wavefront
   constexpr int WAVES_M = BM / WROWS, WAVES_N = kWaves / WAVES_M;
   constexpr int OUT_N = GATED ? BN / 2 : BN;  // output columns per tile
@@ -143,6 +146,9 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
   constexpr int EP = (BM * OUT_N * 2 > STAGE * STAGES) ? 2 : 1;
   static_assert(BM * OUT_N * 2 <= EP * STAGE * STAGES && WAVES_N % EP == 0, "epilogue passes");
   static_assert(!GATED || (B_LOADS % 2 == 0), "gated B loads split evenly");
+  // a tile's B rows lie in one packed row block (OUT_N 256 only where N % 256 == 0)
+  static_assert(!BLOCKED || (BK == kPackedSlice && (OUT_N == 128 || OUT_N == 256)),
+                "packed B tiles");
 
   __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE];
   __shared__ int mt_prefix[kMaxExperts + 1];
@@ -231,15 +237,30 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
     // scalar bases + 32-bit per-lane offsets (elements) within the tile
     const uint16_t* a_base = g.a + row0 * K;
     const int ldb = g.ldb;
-    const uint16_t* b_base0 = g.b0 + (int64_t(e) * N + int64_t(nt) * OUT_N) * ldb;
-    const uint16_t* b_base1 = (GATED || KIND == kKSplit)
-                                  ? g.b1 + (int64_t(e) * N + int64_t(nt) * OUT_N) * ldb
-                                  : b_base0;
+    // B: the tile's OUT_N output rows of expert e. Blocked (packed) weights
+    // hold each K-slice of those rows in one contiguous run; row-major ones
+    // hold each row's K values contiguously, ldb apart.
+    int64_t b_off;
+    uint32_t b_bytes, b_step, b_row;
+    if constexpr (BLOCKED) {
+      const int R = packed_row_block(N), n0 = nt * OUT_N;
+      b_off = int64_t(e) * N * K + int64_t(n0 / R) * K * R + int64_t(n0 % R) * BK;
+      b_bytes = uint32_t(int64_t(K) * R - int64_t(n0 % R) * BK) * 2u;
+      b_step = uint32_t(R) * BK;  // elements from one K-slice to the next
+      b_row = BK;
+    } else {
+      b_off = (int64_t(e) * N + int64_t(nt) * OUT_N) * ldb;
+      b_bytes = uint32_t(OUT_N) * uint32_t(ldb) * 2u;
+      b_step = BK;
+      b_row = uint32_t(ldb);
+    }
+    const uint16_t* b_base0 = g.b0 + b_off;
+    const uint16_t* b_base1 = (GATED || KIND == kKSplit) ? g.b1 + b_off : b_base0;
     // A's range ends at the expert's last valid row of the tile: the rows
     // past it read as zeros (their results are never stored)
     const i32x4 ra = make_rsrc(a_base, uint32_t(rows_valid) * uint32_t(K) * 2u);
-    const i32x4 rb0 = make_rsrc(b_base0, uint32_t(OUT_N) * uint32_t(ldb) * 2u);
-    const i32x4 rb1 = make_rsrc(b_base1, uint32_t(OUT_N) * uint32_t(ldb) * 2u);
+    const i32x4 rb0 = make_rsrc(b_base0, b_bytes);
+    const i32x4 rb1 = make_rsrc(b_base1, b_bytes);
     uint32_t oa[A_LOADS], ob[B_LOADS];
 #pragma unroll
     for (int i = 0; i < A_LOADS; ++i) {
@@ -249,7 +270,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
 #pragma unroll
     for (int i = 0; i < B_LOADS; ++i) {
       const int r = (wid + kWaves * i) * RB + ld_r;  // gated: first half gate rows, then up
-      ob[i] = uint32_t(GATED ? r % (BN / 2) : r) * uint32_t(ldb) + ld_ch * 8;
+      ob[i] = uint32_t(GATED ? r % (BN / 2) : r) * b_row + ld_ch * 8;
     }
     auto issue = [&](int kt, int st) {
       const uint32_t sbase = lds0 + st * STAGE;
@@ -267,7 +288,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
       } else {
 #pragma unroll
         for (int i = 0; i < B_LOADS; ++i)
-          dma16((GATED && i >= B_LOADS / 2) ? rb1 : rb0, (ob[i] + k0) * 2,
+          dma16((GATED && i >= B_LOADS / 2) ? rb1 : rb0, (ob[i] + uint32_t(kt) * b_step) * 2,
                 sbase + A_BYTES + (wid + kWaves * i) * 1024);
       }
     };

@@ -179,6 +179,7 @@ int32_t moe_pack_weights(const void* w_d, int64_t num_mats, int32_t rows, int32_
   if (num_mats < 0 || num_mats > 65535 || rows < 0 || cols < 0) return MOE_ERR_ARG;
   if (num_mats == 0 || rows == 0 || cols == 0) return MOE_OK;
   if (!w_d || !wt_d || w_d == wt_d) return MOE_ERR_ARG;
+  if (rows % 128 || cols % 128) return MOE_ERR_UNSUPPORTED;
   return status_of(moe::launch_pack(w_d, num_mats, rows, cols, wt_d, as_stream(stream)));
 }
 

@@ -131,6 +131,16 @@ hipError_t launch_combine_backward(const void* grad_out, const void* y, int64_t 
 hipError_t launch_route_backward(const int32_t* topk_idx, const float* topk_w,
                                  const float* grad_w, int64_t T, int E, int k,
                                  float* grad_logits, hipStream_t s);
+// Packed expert-weight layout (written by launch_pack, read by the forward
+// grouped GEMMs): for each matrix, its N output rows form blocks of
+// R = packed_row_block(N) rows, and each block is stored as K / kPackedSlice
+// consecutive [R][kPackedSlice] slices, so one K-slice of up to R rows of a
+// block is a single contiguous run. Element (n, k) of matrix m sits at
+//   m*N*K + (n / R) * K * R + (k / kPackedSlice) * R * kPackedSlice
+//         + (n % R) * kPackedSlice + k % kPackedSlice.
+constexpr int kPackedSlice = 64;
+__host__ __device__ constexpr int packed_row_block(int n) { return n % 256 == 0 ? 256 : 128; }
+
 hipError_t launch_pack(const void* w, int64_t mats, int rows, int cols, void* wt, hipStream_t s);
 
 hipError_t launch_gate_up(const void* x_perm, const int32_t* offsets, const int32_t* counts,

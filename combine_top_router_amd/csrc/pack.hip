@@ -1,9 +1,12 @@
-// One-time weight repack: wt[m, c, r] = w[m, r, c] (bf16 bit copy), turning
-// math-orientation expert matrices into the output-major, reduction-
-// contiguous layout the grouped GEMM streams (the load-time conversion into
-// the grouped expert layout, DeepSpeed AutoEP commit text, section "Design":
-// ep_repack.py). 64x64 tiles through LDS so both the read and the write are
-// row-contiguous.
+// One-time weight repack: math-orientation expert matrices w[m, r, c]
+// (r < rows = K, the reduction dimension; c < cols = N, the output dimension)
+// become the packed layout the forward grouped GEMMs stream (the load-time
+// conversion into the grouped expert layout, DeepSpeed AutoEP commit text,
+// section "Design": ep_repack.py): output-major with K contiguous, and the N
+// rows cut into blocks of packed_row_block(N) rows whose K-slices of
+// kPackedSlice values are each one contiguous run, so a GEMM tile's B slice
+// is a single sequential read. A bf16 bit copy: 64x64 tiles through LDS, so
+// the reads are row-contiguous and the writes 128-byte runs.
 #include "moe_internal.h"
 
 namespace moe {
@@ -13,11 +16,14 @@ constexpr int kT = 64;
 
 __global__ __launch_bounds__(256) void pack_kernel(const uint16_t* __restrict__ w, int rows,
                                                    int cols, uint16_t* __restrict__ wt) {
+  static_assert(kT == kPackedSlice, "one tile column is one packed K-slice");
   __shared__ uint16_t tile[kT][kT + 2];
   const int64_t m = blockIdx.z;
   const int r0 = blockIdx.y * kT, c0 = blockIdx.x * kT;
+  const int R = packed_row_block(cols);
   const uint16_t* src = w + m * int64_t(rows) * cols;
-  uint16_t* dst = wt + m * int64_t(rows) * cols;
+  // this tile's K-slice r0 / kT of the row blocks
+  uint16_t* dst = wt + m * int64_t(rows) * cols + int64_t(r0 / kT) * R * kT;
   const int tx = threadIdx.x % kT, ty = threadIdx.x / kT;  // 64 x 4
   for (int i = ty; i < kT; i += 4) {
     const int r = r0 + i, c = c0 + tx;
@@ -26,7 +32,8 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint16_t* __restrict__ 
   __syncthreads();
   for (int i = ty; i < kT; i += 4) {
     const int c = c0 + i, r = r0 + tx;
-    if (r < rows && c < cols) dst[int64_t(c) * rows + r] = tile[tx][i];
+    if (r < rows && c < cols)
+      dst[int64_t(c / R) * rows * R + (c % R) * kT + tx] = tile[tx][i];
   }
 }
 

@@ -150,7 +150,11 @@ def permute(x: torch.Tensor, dst_row: torch.Tensor, m_cap: int, out=None) -> tor
 # ---------------------------------------------------------------- experts
 
 def pack_weights(w: torch.Tensor, out=None) -> torch.Tensor:
-    """[n, R, C] bf16 -> [n, C, R] (each matrix transposed), the GEMM's layout."""
+    """Math-orientation [n, K, N] bf16 matrices -> the packed layout the forward
+    grouped GEMMs read (moe_pack_weights): output-major, N rows in blocks of 256
+    (128 if N % 256), each block stored as K/64 contiguous [block][64] slices.
+    Returned with shape [n, N, K]; only its element order differs from the
+    plain transpose."""
     _need(w, "w", torch.bfloat16)
     n, R, Cc = w.shape
     out = _empty((n, Cc, R), torch.bfloat16, w.device) if out is None else out
@@ -169,7 +173,8 @@ def _gemm_common(a, offsets, counts):
 
 
 def grouped_gate_up(x_perm, offsets, counts, w1t, w3t, out=None):
-    """h = silu(x W1) * (x W3) per local expert group; w1t/w3t are [E_loc, I, H]."""
+    """h = silu(x W1) * (x W3) per local expert group; w1t/w3t are W1/W3 [E_loc, H, I]
+    after pack_weights (shape [E_loc, I, H])."""
     e_loc = _gemm_common(x_perm, offsets, counts)
     m_cap, H = x_perm.shape
     I = w1t.shape[1]
@@ -184,7 +189,8 @@ def grouped_gate_up(x_perm, offsets, counts, w1t, w3t, out=None):
 
 
 def grouped_down(h, offsets, counts, w2t, out=None):
-    """y = h W2 per local expert group; w2t is [E_loc, H, I]."""
+    """y = h W2 per local expert group; w2t is W2 [E_loc, I, H] after pack_weights
+    (shape [E_loc, H, I])."""
     e_loc = _gemm_common(h, offsets, counts)
     m_cap, I = h.shape
     H = w2t.shape[1]

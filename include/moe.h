@@ -195,15 +195,21 @@ int32_t moe_permute_weighted(const void* x_d, int64_t num_tokens, int32_t hidden
                              void* x_perm_d, void* stream);
 
 /*
- * moe_pack_weights -- one-time repack of expert matrices to the layout the
- * grouped GEMM reads: wt[e, c, r] = w[e, r, c] for e < num_mats, a bit copy.
- * Expert weights arrive in math orientation (gate/up [E, H, I], down
- * [E, I, H]); the GEMM wants each expert's matrix output-major with the
- * reduction dimension contiguous (gate/up [E, I, H], down [E, H, I]). This is
- * the load-time conversion into the grouped expert layout the runtime
- * expects (DeepSpeed AutoEP commit text, section "Design": ep_repack.py),
- * done once per weight set, outside the per-step path.
- *   w_d  [num_mats, rows, cols] bf16;  wt_d [num_mats, cols, rows] bf16 (out)
+ * moe_pack_weights -- one-time repack of expert matrices into the packed
+ * layout the forward grouped GEMMs read (moe_grouped_gate_up, _gate_up_save,
+ * _down, _swiglu). This is the load-time conversion into the grouped expert
+ * layout the runtime expects (DeepSpeed AutoEP commit text, section "Design":
+ * ep_repack.py), done once per weight set, outside the per-step path; the
+ * layout itself is this library's. Expert weights arrive in math orientation
+ * w[m, k, n] (gate/up [E, H, I], down [E, I, H]; k the reduction index, n the
+ * output index, K = rows, N = cols). The packed matrix is output-major with
+ * the N rows cut into blocks of R = 256 rows if N % 256 == 0, else 128, and
+ * each block stored as K/64 consecutive [R][64] slices:
+ *   wt[m*N*K + (n/R)*K*R + (k/64)*R*64 + (n%R)*64 + k%64] = w[m, k, n]
+ * (a bf16 bit copy; wt has the element count of w).
+ *   w_d  [num_mats, rows, cols] bf16;  wt_d (out), num_mats * rows * cols bf16
+ * rows and cols multiples of 128, else MOE_ERR_UNSUPPORTED; w_d and wt_d
+ * distinct (MOE_ERR_ARG otherwise).
  */
 int32_t moe_pack_weights(const void* w_d, int64_t num_mats, int32_t rows, int32_t cols,
                          void* wt_d, void* stream);
@@ -227,7 +233,8 @@ int32_t moe_pack_weights(const void* w_d, int64_t num_mats, int32_t rows, int32_
  *   x_perm_d   [m_cap, H] bf16          h_d [m_cap, I] bf16        y_d [m_cap, H] bf16
  *   offsets_d  [E_loc + 1] int32        counts_d [E_loc] int32 (local expert counts,
  *                                       = expert_counts_d + first local expert)
- *   w1t_d, w3t_d [E_loc, I, H] bf16     w2t_d [E_loc, H, I] bf16  (moe_pack_weights layout)
+ *   w1t_d, w3t_d: W1, W3 packed by moe_pack_weights (rows H, cols I), E_loc * I * H bf16
+ *   w2t_d: W2 packed by moe_pack_weights (rows I, cols H), E_loc * H * I bf16
  * Limits: H and I multiples of 128; E_loc <= 1024; offsets[E_loc] <= m_cap.
  * All bf16 pointers 16-byte aligned. Unsupported shapes: MOE_ERR_UNSUPPORTED.
  */
@@ -263,7 +270,7 @@ int32_t moe_grouped_swiglu(const void* x_perm_d, const int32_t* offsets_d,
  *                                 the 2I products), rounded to bf16
  *
  *   x_perm_d, dy_d, dx_perm_d [m_cap, H] bf16;  h_d [m_cap, I];  gu_d, dgu_d [m_cap, 2I]
- *   w1t_d, w3t_d [E_loc, I, H] (moe_pack_weights layout, forward only)
+ *   w1t_d, w3t_d: W1, W3 packed by moe_pack_weights (forward only)
  *   w1_d, w3_d [E_loc, H, I], w2_d [E_loc, I, H]: the math-orientation weights, which
  *   are already output-major for the backward products
  * Rows outside the expert groups are neither read nor written. Limits as the

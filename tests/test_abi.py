@@ -107,3 +107,5 @@ def test_argument_checks_return_before_launch(lib):
     assert lib.moe_grouped_gate_up(fake, fake, fake, 0, 1024, 128, 256, fake, fake, fake,
                                    None) == 1
     assert lib.moe_pack_weights(fake, 2, 4, 4, fake, None) == 1                 # in place
+    assert lib.moe_pack_weights(fake, 2, 64, 128, odd, None) == 2               # K % 128
+    assert lib.moe_pack_weights(fake, 2, 128, 192, odd, None) == 2              # N % 128

@@ -283,11 +283,28 @@ def test_grouped_swiglu(name, dist, share):
         assert (bits(y[torch.as_tensor(pad, device="cuda")]) == 0x7FC1).all()
 
 
-def test_pack_weights_is_a_transpose():
-    announce("pack")
-    w = torch.randn((3, 384, 256), device="cuda").to(torch.bfloat16)
+def packed_reference(w: np.ndarray) -> np.ndarray:
+    """The packed layout written out from its definition in include/moe.h:
+    output-major [m, N, K], N rows in blocks of R (256 if N % 256 == 0, else
+    128), each block as K/64 consecutive [R][64] slices."""
+    m, K, N = w.shape
+    R = 256 if N % 256 == 0 else 128
+    out = np.empty(m * N * K, dtype=w.dtype)
+    for n in range(N):
+        for k0 in range(0, K, 64):
+            base = (n // R) * K * R + (k0 // 64) * R * 64 + (n % R) * 64
+            for mm in range(m):
+                out[mm * N * K + base: mm * N * K + base + 64] = w[mm, k0:k0 + 64, n]
+    return out
+
+
+@pytest.mark.parametrize("shape", [(3, 384, 256), (2, 256, 384), (1, 128, 128)])
+def test_pack_weights_layout(shape):
+    announce(f"pack {shape}")
+    w = torch.randn(shape, device="cuda").to(torch.bfloat16)
     wt = moe.pack_weights(w)
-    assert (bits(wt) == bits(w).transpose(0, 2, 1)).all()
+    assert tuple(wt.shape) == (shape[0], shape[2], shape[1])
+    assert (bits(wt).reshape(-1) == packed_reference(bits(w))).all()
 
 
 def test_swiglu_orientation_closed_form():

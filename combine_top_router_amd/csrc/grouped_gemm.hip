@@ -154,7 +154,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
   __shared__ int mt_prefix[kMaxExperts + 1];
   __shared__ int wave_tot[kWaves];
 
-  const int tid = threadIdx.x, lane = lane_id(), wid = tid / kWave;
+  // the wavefront index in a scalar register: LDS destinations are scalar arithmetic
+  const int tid = threadIdx.x, lane = lane_id(), wid = uniform(tid / kWave);
   const int wm = wid / WAVES_N, wn = wid % WAVES_N;
   const int K = g.k, N = g.n;
   const int NT = N / OUT_N, KT = K / BK;
@@ -261,34 +262,35 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
     const i32x4 ra = make_rsrc(a_base, uint32_t(rows_valid) * uint32_t(K) * 2u);
     const i32x4 rb0 = make_rsrc(b_base0, b_bytes);
     const i32x4 rb1 = make_rsrc(b_base1, b_bytes);
+    // per-lane byte offsets of the first K-slice (fixed for the tile); each
+    // slice adds a wave-uniform advance
     uint32_t oa[A_LOADS], ob[B_LOADS];
 #pragma unroll
     for (int i = 0; i < A_LOADS; ++i) {
       const int r = (wid + kWaves * i) * RB + ld_r;
-      oa[i] = uint32_t(r) * uint32_t(K) + ld_ch * 8;
+      oa[i] = (uint32_t(r) * uint32_t(K) + ld_ch * 8) * 2u;
     }
 #pragma unroll
     for (int i = 0; i < B_LOADS; ++i) {
       const int r = (wid + kWaves * i) * RB + ld_r;  // gated: first half gate rows, then up
-      ob[i] = uint32_t(GATED ? r % (BN / 2) : r) * b_row + ld_ch * 8;
+      ob[i] = (uint32_t(GATED ? r % (BN / 2) : r) * b_row + ld_ch * 8) * 2u;
     }
     auto issue = [&](int kt, int st) {
       const uint32_t sbase = lds0 + st * STAGE;
       const uint32_t k0 = uint32_t(kt) * BK;
 #pragma unroll
-      for (int i = 0; i < A_LOADS; ++i)
-        dma16(ra, (oa[i] + k0) * 2, sbase + (wid + kWaves * i) * 1024);
+      for (int i = 0; i < A_LOADS; ++i) dma16(ra, oa[i], k0 * 2, sbase + (wid + kWaves * i) * 1024);
       if constexpr (KIND == kKSplit) {
         // the same slice of b0 or, past k_split, of b1 (slices never straddle it)
         const bool second = k0 >= uint32_t(g.k_split);
         const uint32_t kb = second ? k0 - uint32_t(g.k_split) : k0;
 #pragma unroll
         for (int i = 0; i < B_LOADS; ++i)
-          dma16(second ? rb1 : rb0, (ob[i] + kb) * 2, sbase + A_BYTES + (wid + kWaves * i) * 1024);
+          dma16(second ? rb1 : rb0, ob[i], kb * 2, sbase + A_BYTES + (wid + kWaves * i) * 1024);
       } else {
 #pragma unroll
         for (int i = 0; i < B_LOADS; ++i)
-          dma16((GATED && i >= B_LOADS / 2) ? rb1 : rb0, (ob[i] + uint32_t(kt) * b_step) * 2,
+          dma16((GATED && i >= B_LOADS / 2) ? rb1 : rb0, ob[i], uint32_t(kt) * b_step * 2,
                 sbase + A_BYTES + (wid + kWaves * i) * 1024);
       }
     };

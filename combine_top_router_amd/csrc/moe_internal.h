@@ -76,6 +76,20 @@ __device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t byte_off, uint32_t ld
                : "memory");
 }
 
+// As dma16, at byte offset voff + soff: a per-lane part that a loop can keep
+// in one register and a wave-uniform part (a K-slice advance) in a scalar
+// register. A loop that recomputes the per-lane register between transfers
+// makes the compiler wait for the transfer that read it (it cannot see that
+// the hardware read the address at issue), so the per-lane parts stay fixed.
+// The buffer range check covers the per-lane part; callers keep soff within
+// the same range (rows past the range are decided by voff alone).
+__device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t voff, uint32_t soff,
+                                      uint32_t lds_addr) {
+  asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(rsrc), "s"(soff),
+               "{m0}"(lds_addr)
+               : "memory");
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");

@@ -74,7 +74,7 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(WgradArgs g) {
 
   __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
 
-  const int tid = threadIdx.x, lane = lane_id(), wid = tid / kWave;
+  const int tid = threadIdx.x, lane = lane_id(), wid = uniform(tid / kWave);
   const int wm = wid / WAVES_N, wn = wid % WAVES_N;
   const int M = g.m, N = g.n;
   const int MT = M / BM, NTL = N / BN, per_expert = MT * NTL;

@@ -68,6 +68,31 @@ def calibrate_copy(mib: int):
     print(json.dumps({"calibrate_copy_bytes": n, "launches": 5}), flush=True)
 
 
+def roof_entry(ms: float, bound: str, amount) -> dict:
+    """Achieved rate of one stage against its roofline. HBM stages carry their
+    algorithmic bytes. GEMM stages carry (flops, bytes), bytes being the least
+    traffic the product needs (each weight of an expert with rows read once,
+    activations read once, outputs written once): the binding ceiling is the
+    lower of the MFMA peak and intensity x HBM peak, so a product below the
+    ridge point (2516.6 TFLOP/s / 8 TB/s = 315 flop/byte) is HBM-bound."""
+    sec = ms * 1e-3
+    if bound == "hbm":
+        ach = amount / sec / 1e9
+        return {"ms": round(ms, 4), "bound": "hbm", "GB/s": round(ach, 1),
+                "frac": round(ach / PEAK_HBM_GBS, 4), "bytes": int(amount)}
+    flops, nbytes = amount
+    tf, gbs = flops / sec / 1e12, nbytes / sec / 1e9
+    intensity = flops / nbytes
+    out = {"ms": round(ms, 4), "TFLOP/s": round(tf, 1), "GB/s": round(gbs, 1),
+           "flops": flops, "bytes": int(nbytes), "flop_per_byte": round(intensity, 1),
+           "mfma_frac": round(tf / PEAK_BF16_TFLOPS, 4), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}
+    if intensity * PEAK_HBM_GBS * 1e9 >= PEAK_BF16_TFLOPS * 1e12:
+        out.update(bound="mfma", frac=round(tf / PEAK_BF16_TFLOPS, 4))
+    else:
+        out.update(bound="hbm", frac=round(gbs / PEAK_HBM_GBS, 4))
+    return out
+
+
 def traffic_record(kernel: str, workload: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it was
     taken on the current kernel source (else None)."""
@@ -177,21 +202,24 @@ def time_backward(args, cfg, layer, moe, stream, t_loc, n_loc, weights, x):
     dl_ep = max(cfg.ep_size, 8) if E % max(cfg.ep_size, 8) == 0 else cfg.ep_size
     sh = workloads.gen.random_rows(cfg, T, torch.bfloat16, args.seed, device=dev)
     nhi = float(n_loc) * H * I
+    e_act = int((L.local_counts > 0).sum().item())
+    wbytes = float(e_act) * H * I * 2  # one expert matrix of each active expert
     calls = [
         ("gate_up_save", lambda: moe.ops.grouped_gate_up_save(
-            layer.x_perm, off, cnt, layer.w1t, layer.w3t, layer.h, gu), "mfma", 4 * nhi),
+            layer.x_perm, off, cnt, layer.w1t, layer.w3t, layer.h, gu), "gemm",
+         (4 * nhi, 2 * wbytes + n_loc * (H + I + 2 * I) * 2)),
         ("combine_backward", lambda: moe.ops.combine_backward(G, layer.y, dst, layer.topk_w, gy, gw),
          "hbm", t_loc * H * 2 + 2 * n_loc * H * 2 + T * k * 12),
         ("route_backward", lambda: moe.ops.route_backward(layer.topk_idx, layer.topk_w, gw, E, gl),
          "hbm", T * E * 4 + T * k * 12),
         ("down_backward", lambda: moe.ops.grouped_down_backward(gy, gu, off, cnt, w2, dgu),
-         "mfma", 2 * nhi),
+         "gemm", (2 * nhi, wbytes + n_loc * (H + 4 * I) * 2)),
         ("down_wgrad", lambda: moe.ops.grouped_down_wgrad(layer.h, gy, off, cnt, dw2),
-         "mfma", 2 * nhi),
+         "gemm", (2 * nhi, float(e_loc) * H * I * 2 + n_loc * (I + H) * 2)),
         ("gate_up_backward", lambda: moe.ops.grouped_gate_up_backward(dgu, off, cnt, w1, w3, dxp),
-         "mfma", 4 * nhi),
+         "gemm", (4 * nhi, 2 * wbytes + n_loc * (2 * I + H) * 2)),
         ("gate_up_wgrad", lambda: moe.ops.grouped_gate_up_wgrad(layer.x_perm, dgu, off, cnt, dw1, dw3),
-         "mfma", 4 * nhi),
+         "gemm", (4 * nhi, 2 * float(e_loc) * H * I * 2 + n_loc * (H + 2 * I) * 2)),
         ("permute_backward", lambda: moe.ops.permute_backward(dxp, dst, gx),
          "hbm", n_loc * H * 2 + T * H * 2 + T * k * 4),
         # restore variants: the shared expert's rows merged, and the permute
@@ -221,14 +249,7 @@ def time_backward(args, cfg, layer, moe, stream, t_loc, n_loc, weights, x):
             ev[r + 1].record(stream)
         torch.cuda.synchronize()
         ms = float(np.mean([ev[r].elapsed_time(ev[r + 1]) for r in range(reps)]))
-        if bound == "hbm":
-            ach = amount / (ms * 1e-3) / 1e9
-            out[name] = {"ms": round(ms, 4), "bound": "hbm", "GB/s": round(ach, 1),
-                         "frac": round(ach / PEAK_HBM_GBS, 4), "bytes": int(amount)}
-        else:
-            ach = amount / (ms * 1e-3) / 1e12
-            out[name] = {"ms": round(ms, 4), "bound": "mfma", "TFLOP/s": round(ach, 1),
-                         "frac": round(ach / PEAK_BF16_TFLOPS, 4), "flops": amount}
+        out[name] = roof_entry(ms, bound, amount)
     return out
 
 
@@ -281,12 +302,13 @@ def main():
     e_act = int((counts > 0).sum())
     T, H, I, E, k = cfg.num_tokens, cfg.hidden, cfg.inter, cfg.num_experts, cfg.top_k
     N = T * k
+    wbytes = float(e_act) * H * I * 2  # one expert matrix of each active expert
     work = {
         "route": ("hbm", T * E * 4 + N * 8),
         "layout": ("hbm", N * 4 * 2 + n_loc * 4),
         "permute": ("hbm", (t_loc + n_loc) * H * 2),
-        "gate_up": ("mfma", 4.0 * n_loc * H * I),
-        "down": ("mfma", 2.0 * n_loc * H * I),
+        "gate_up": ("gemm", (4.0 * n_loc * H * I, 2 * wbytes + n_loc * (H + I) * 2)),
+        "down": ("gemm", (2.0 * n_loc * H * I, wbytes + n_loc * (I + H) * 2)),
         "combine": ("hbm", n_loc * H * 2 + N * 8 + T * H * 2),
     }
 
@@ -310,20 +332,10 @@ def main():
     tokens_per_step = T // cfg.ep_size
     value = tokens_per_step * args.steps / elapsed
 
-    stage_out = {}
-    for name, ms in stage_ms.items():
-        bound, amount = work[name]
-        if bound == "hbm":
-            ach = amount / (ms * 1e-3) / 1e9
-            stage_out[name] = {"ms": round(ms, 4), "bound": "hbm", "GB/s": round(ach, 1),
-                               "frac": round(ach / PEAK_HBM_GBS, 4), "bytes": int(amount)}
-        else:
-            ach = amount / (ms * 1e-3) / 1e12
-            stage_out[name] = {"ms": round(ms, 4), "bound": "mfma", "TFLOP/s": round(ach, 1),
-                               "frac": round(ach / PEAK_BF16_TFLOPS, 4), "flops": amount}
+    stage_out = {name: roof_entry(ms, *work[name]) for name, ms in stage_ms.items()}
     dom = max(stage_ms, key=stage_ms.get)
     d = stage_out[dom]
-    traffic = traffic_record(dom, cfg.name) if d["bound"] == "mfma" else None
+    traffic = traffic_record(dom, cfg.name) if dom in ("gate_up", "down") else None
     if d["bound"] == "mfma":
         roof = {"bound": "mfma", "kernel": dom, "achieved": d["TFLOP/s"],
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": d["frac"],

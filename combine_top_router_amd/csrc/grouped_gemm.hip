@@ -51,6 +51,7 @@
 //    a tile larger than the stage buffers goes out in two column passes.
 #include <algorithm>
 #include <type_traits>
+#include <utility>
 
 #include "moe_internal.h"
 
@@ -108,6 +109,22 @@ __device__ __forceinline__ int swz_key(int row) {
 template <int BK>
 __device__ __forceinline__ int swz(int row, int ch) {
   return row * (BK * 2) + ((ch ^ swz_key<BK>(row)) << 4);
+}
+
+// Instruction-scheduling hint for one 16-wide K step with NR fragment reads
+// (LDS) and NM matrix products: read slot T is preceded by one or two
+// products, so the reads for the next step spread over this step's products
+// instead of bunching up in front of them.
+template <int T, int NR, int NM>
+__device__ __forceinline__ void interleave_slot() {
+  constexpr int PRE = NM > NR ? NM - NR : 0;  // slots that take two products
+  constexpr int M = T < PRE ? 2 : (T - PRE < NM - 2 * PRE ? 1 : 0);
+  if constexpr (M > 0) __builtin_amdgcn_sched_group_barrier(0x008, M, 0);  // MFMA
+  __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                        // LDS read
+}
+template <int NR, int NM, int... T>
+__device__ __forceinline__ void interleave_reads(std::integer_sequence<int, T...>) {
+  (interleave_slot<T, NR, NM>(), ...);
 }
 
 // Calls f(std::integral_constant<int, nb>) for the run-time nb in 0..NB, so
@@ -318,11 +335,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
       bf16x8 fa[2][TM], fb[2][TN];
       auto read_frags = [&](const char* base, int kk, bf16x8 (&a)[TM], bf16x8 (&b)[TN]) {
         const int ch = 2 * kk + (lane >> 5);
-#pragma unroll
-        for (int i = 0; i < NB; ++i)
-          a[i] = *reinterpret_cast<const bf16x8*>(
-              base + swz<BK>(wm * WROWS + i * 32 + (lane & 31), ch));
         if (NB == 0) return;
+        // B first: a step's first products need both B fragments and A[0]
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
           const int brow = GATED ? (j / HALF) * (BN / 2) + wn * WCOL + (j % HALF) * 32
@@ -330,6 +344,10 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
           b[j] = *reinterpret_cast<const bf16x8*>(base + A_BYTES +
                                                   swz<BK>(brow + (lane & 31), ch));
         }
+#pragma unroll
+        for (int i = 0; i < NB; ++i)
+          a[i] = *reinterpret_cast<const bf16x8*>(
+              base + swz<BK>(wm * WROWS + i * 32 + (lane & 31), ch));
       };
       auto mfma = [&](const bf16x8 (&a)[TM], const bf16x8 (&b)[TN]) {
 #pragma unroll
@@ -352,6 +370,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
         for (int kk = 0; kk + 1 < KK; ++kk) {
           read_frags(base, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
           mfma(fa[kk & 1], fb[kk & 1]);
+          // interleave the next step's fragment reads with this step's products
+          if constexpr (NB > 0) interleave_reads<NB + TN, NB * TN>(std::make_integer_sequence<int, NB + TN>{});
         }
         if (kt + 1 < KT) {
           // slice kt+1 landed (this wavefront's part), and all of slice kt is read

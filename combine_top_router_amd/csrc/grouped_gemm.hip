@@ -395,57 +395,48 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
     // columns.
     uint16_t* ct = reinterpret_cast<uint16_t*>(smem);
     if constexpr (KIND == kSwigluBwd) {
-      // one pass per wavefront column (PN = WCOL columns): the forward's g and
-      // u of the pass's columns are staged in LDS with 16-byte loads, then
-      // each output (dg, du) goes out through a third LDS tile
+      // one pass per wavefront column (PN = WCOL columns): that column's dh
+      // (fp32) goes to LDS in the accumulator layout, then every thread takes
+      // 8 consecutive columns of a row: the forward's g and u come in with
+      // 16-byte loads, dg and du go out with 16-byte stores
       constexpr int PN = WCOL, OCH = PN / 8;
-      static_assert(3 * BM * PN * 2 <= STAGE * STAGES, "g, u and output tiles fit the stages");
-      uint16_t* gt = ct + BM * PN;
-      uint16_t* ut = gt + BM * PN;
+      constexpr int PS = PN + 8;  // fp32 row stride: rows 4 apart land 32 banks apart
+      static_assert(BM * PS * 4 <= STAGE * STAGES, "dh tile fits the stages");
+      float* dt = reinterpret_cast<float*>(smem);
       for (int pass = 0; pass < WAVES_N; ++pass) {
+        if (wn == pass) {
+#pragma unroll
+          for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+              for (int q = 0; q < 16; ++q) {
+                const int r = wm * WROWS + i * 32 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
+                dt[r * PS + j * 32 + (lane & 31)] = acc[i][j][q];
+              }
+        }
+        __syncthreads();
         const int64_t cb = int64_t(nt) * OUT_N + pass * PN;  // first column of the pass
         for (int c = tid; c < rows_valid * OCH; c += kThreads) {
           const int r = c / OCH, ch = c % OCH;
-          const uint16_t* src = g.aux + (row0 + r) * 2 * int64_t(N) + cb + ch * 8;
-          *reinterpret_cast<u32x4*>(gt + r * PN + ch * 8) = *reinterpret_cast<const u32x4*>(src);
-          *reinterpret_cast<u32x4*>(ut + r * PN + ch * 8) = *reinterpret_cast<const u32x4*>(src + N);
+          const int64_t off = (row0 + r) * 2 * int64_t(N) + cb + ch * 8;
+          float gg[8], uu[8];
+          unpack8(*reinterpret_cast<const u32x4*>(g.aux + off), gg);
+          unpack8(*reinterpret_cast<const u32x4*>(g.aux + off + N), uu);
+          const f32x4 d0 = *reinterpret_cast<const f32x4*>(dt + r * PS + ch * 8);
+          const f32x4 d1 = *reinterpret_cast<const f32x4*>(dt + r * PS + ch * 8 + 4);
+          const float dh[8] = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
+          float dg[8], du[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-gg[e]));
+            dg[e] = dh[e] * uu[e] * (sg * (1.0f + gg[e] * (1.0f - sg)));
+            du[e] = dh[e] * (gg[e] * sg);
+          }
+          *reinterpret_cast<u32x4*>(g.c + off) = pack8(dg);
+          *reinterpret_cast<u32x4*>(g.c + off + N) = pack8(du);
         }
-        __syncthreads();
-        // output O (compile time): dg, then du
-        auto emit = [&](auto o_tag) __attribute__((always_inline)) {
-          constexpr int O = decltype(o_tag)::value;
-          if (wn == pass) {
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-#pragma unroll
-              for (int j = 0; j < TN; ++j)
-#pragma unroll
-                for (int q = 0; q < 16; ++q) {
-                  const int r = wm * WROWS + i * 32 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
-                  const int col = j * 32 + (lane & 31);  // within the pass
-                  // rows past rows_valid hold stale LDS: their results are never stored
-                  const float dh = acc[i][j][q];
-                  const float gg = from_bf16(gt[r * PN + col]);
-                  const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-gg));
-                  float v;
-                  if constexpr (O == 0)
-                    v = dh * from_bf16(ut[r * PN + col]) * (sg * (1.0f + gg * (1.0f - sg)));
-                  else
-                    v = dh * (gg * sg);
-                  ct[r * PN + col] = to_bf16(v);
-                }
-          }
-          __syncthreads();
-          uint16_t* C = g.c + row0 * 2 * int64_t(N) + O * int64_t(N) + cb;
-          for (int c = tid; c < rows_valid * OCH; c += kThreads) {
-            const int r = c / OCH, ch = c % OCH;
-            *reinterpret_cast<u32x4*>(C + int64_t(r) * 2 * N + ch * 8) =
-                *reinterpret_cast<const u32x4*>(ct + r * PN + ch * 8);
-          }
-          __syncthreads();  // ct (and, after du, gt/ut) read out before the next write
-        };
-        emit(std::integral_constant<int, 0>{});
-        emit(std::integral_constant<int, 1>{});
+        __syncthreads();  // dt read out before the next pass writes it
       }
     } else {
       constexpr int NOUT = KIND == kGatedSave ? 3 : 1;
@@ -552,8 +543,7 @@ hipError_t launch_down_backward(const void* dy, const void* gu, const int32_t* o
   a.c = static_cast<uint16_t*>(dgu);
   a.aux = static_cast<const uint16_t*>(gu);
   a.offsets = offsets, a.counts = counts, a.e_loc = e_loc, a.n = I, a.k = H, a.ldb = H;
-  // 256 x 128 tiles: with 320-row tiles the SwiGLU-backward epilogue's
-  // registers spill inside the K loop
+  if (I % 256 == 0) return launch<320, 256, 64, 2, kSwigluBwd, 5>(a, s);
   return launch<256, 128, 64, 2, kSwigluBwd, 2>(a, s);
 }
 

@@ -170,6 +170,9 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE];
   __shared__ int mt_prefix[kMaxExperts + 1];
   __shared__ int wave_tot[kWaves];
+  // each local expert's row count and first row, read once: per-tile reads
+  // from memory would wait (vmcnt) for the previous tile's output stores
+  __shared__ int cnt_s[kMaxExperts], off_s[kMaxExperts];
 
   // the wavefront index in a scalar register: LDS destinations are scalar arithmetic
   const int tid = threadIdx.x, lane = lane_id(), wid = uniform(tid / kWave);
@@ -184,7 +187,9 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
 #pragma unroll
     for (int q = 0; q < PER; ++q) {
       const int e = tid * PER + q;
-      v[q] = e < g.e_loc ? (g.counts[e] + BM - 1) / BM : 0;
+      const int c = e < g.e_loc ? g.counts[e] : 0;
+      if (e < g.e_loc) cnt_s[e] = c, off_s[e] = g.offsets[e];
+      v[q] = (c + BM - 1) / BM;
       run += v[q];
     }
     int incl = run;
@@ -239,7 +244,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
     // (heights differ by at most one block, nothing is computed past the last
     // block); the others give every tile the same height, the last one
     // holding what is left (measured faster for them).
-    const int cnt_e = uniform(g.counts[e]);
+    const int cnt_e = uniform(cnt_s[e]);
     int hgt, start;
     if constexpr (GATED) {
       const int blks = (cnt_e + 31) / 32, bq = blks / mtiles, br = blks % mtiles;
@@ -249,7 +254,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
       hgt = ((cnt_e + mtiles - 1) / mtiles + 31) / 32 * 32;
       start = mt * hgt;
     }
-    const int64_t row0 = int64_t(uniform(g.offsets[e])) + start;
+    const int64_t row0 = int64_t(uniform(off_s[e])) + start;
     const int rows_valid = min(hgt, cnt_e - start);
 
     // scalar bases + 32-bit per-lane offsets (elements) within the tile

@@ -33,6 +33,7 @@ namespace {
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * kWave;
 constexpr int BK = 64;  // rows of the reduction per slice
+constexpr int kMaxExperts = 1024;  // local experts the entry points accept
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
@@ -73,11 +74,16 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(WgradArgs g) {
   static_assert(BM * WCOL * 2 <= 2 * STAGE, "epilogue pass fits the stages");
 
   __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+  // each local expert's row count and first row, read once: per-tile reads
+  // from memory would wait (vmcnt) for the previous tile's output stores
+  __shared__ int cnt_s[kMaxExperts], off_s[kMaxExperts];
 
   const int tid = threadIdx.x, lane = lane_id(), wid = uniform(tid / kWave);
   const int wm = wid / WAVES_N, wn = wid % WAVES_N;
   const int M = g.m, N = g.n;
   const int MT = M / BM, NTL = N / BN, per_expert = MT * NTL;
+  for (int e = threadIdx.x; e < g.e_loc; e += kThreads) cnt_s[e] = g.counts[e], off_s[e] = g.offsets[e];
+  __syncthreads();
   const int total = g.e_loc * per_expert;
   const int G = gridDim.x;
   int slot = blockIdx.x;
@@ -91,8 +97,8 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(WgradArgs g) {
     const int e = tile / per_expert;
     const int rem = tile - e * per_expert;
     const int mt = rem / NTL, nt = rem - mt * NTL;
-    const int cnt = uniform(g.counts[e]);
-    const int64_t base = int64_t(uniform(g.offsets[e]));
+    const int cnt = uniform(cnt_s[e]);
+    const int64_t base = int64_t(uniform(off_s[e]));
     const int KT = (cnt + BK - 1) / BK;
     const int m0 = mt * BM, n0 = nt * BN;
 

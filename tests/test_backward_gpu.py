@@ -178,6 +178,10 @@ EXPERT_SHAPES = {
     "wide_i": (MoEConfig(name="wide_i_bwd", num_tokens=512, hidden=256, num_experts=4,
                          top_k=2, inter=640, align=32), -1, None),
     "deepseek_share": (workloads.get("deepseek_v3_ep8_share"), 0, 3),
+    # ~1024 rows per expert: several 320-row m-tiles per expert on the 320x256
+    # kinds (H and I multiples of 256), the last one short
+    "tall": (MoEConfig(name="tall_bwd", num_tokens=2048, hidden=256, num_experts=4, top_k=2,
+                       inter=256, align=128), -1, None),
     # 64 tokens, top-1 of 32 experts under severe skew: several experts get no
     # rows and must come back with zero weight gradients
     "empty_experts": (MoEConfig(name="empty_bwd", num_tokens=64, hidden=128, num_experts=32,

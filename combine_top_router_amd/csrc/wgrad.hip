@@ -24,7 +24,8 @@
 // K slice (padding rows between experts hold stale data). An expert with no
 // rows gets a zero gradient. Workgroups are persistent; each XCD takes a
 // contiguous range of tile ids (expert-major), so the tiles of one expert,
-// which share both operands, sit behind the same L2.
+// which share both operands, sit behind the same L2. The next tile's first
+// slice is put in flight before a tile's epilogue.
 #include "moe_internal.h"
 
 namespace moe {
@@ -71,7 +72,7 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(WgradArgs g) {
   static_assert(WAVES_M * WAVES_N == kWaves && TN >= 1 && WCOL % 32 == 0, "wavefront grid");
   static_assert(A_LOADS * 1024 * kWaves == A_BYTES && B_LOADS * 1024 * kWaves == B_BYTES,
                 "whole wave-loads");
-  static_assert(BM * WCOL * 2 <= 2 * STAGE, "epilogue pass fits the stages");
+  static_assert(BM * WCOL * 2 <= STAGE, "an epilogue pass fits stage 0");
 
   __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
   // each local expert's row count and first row, read once: per-tile reads
@@ -93,6 +94,10 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(WgradArgs g) {
   // fragment-read coordinates of this lane: group of 16, row quad r, column quad q
   const int grp = lane >> 4, fr = (lane >> 2) & 3, fq = lane & 3;
 
+  // A tile whose first K slice the previous tile put in flight (into stage 1,
+  // before its epilogue, which stages through stage 0 only): its slices then
+  // live in stage (kt + 1) & 1.
+  bool pf = false;
   for (int tile = slot; tile < total; tile += G) {
     const int e = tile / per_expert;
     const int rem = tile - e * per_expert;
@@ -162,15 +167,16 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(WgradArgs g) {
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
     };
 
+    const int sp = pf ? 1 : 0;  // stage of slice 0
     if (KT > 0) {
       bf16x8 fa[2][TM], fb[2][TN];
-      issue(0, 0);
+      if (!pf) issue(0, 0);
       wait_vmcnt<0>();
       __syncthreads();  // slice 0 visible
-      if (KT > 1) issue(1, 1);
-      read_frags(smem, 0, fa[0], fb[0]);
+      if (KT > 1) issue(1, (1 + sp) & 1);
+      read_frags(smem + sp * STAGE, 0, fa[0], fb[0]);
       for (int kt = 0; kt < KT; ++kt) {
-        const char* sb = smem + (kt & 1) * STAGE;
+        const char* sb = smem + ((kt + sp) & 1) * STAGE;
 #pragma unroll
         for (int kk = 0; kk < 3; ++kk) {
           read_frags(sb, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
@@ -179,13 +185,48 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(WgradArgs g) {
         if (kt + 1 < KT) {
           wait_vmcnt<0>();  // slice kt+1 landed (this wavefront's part)
           __syncthreads();  // ... everyone's, and slice kt is read
-          if (kt + 2 < KT) issue(kt + 2, kt & 1);
-          read_frags(smem + ((kt + 1) & 1) * STAGE, 0, fa[0], fb[0]);
+          if (kt + 2 < KT) issue(kt + 2, (kt + sp) & 1);
+          read_frags(smem + ((kt + 1 + sp) & 1) * STAGE, 0, fa[0], fb[0]);
         }
         mfma(fa[1], fb[1]);
       }
     }
     __syncthreads();  // the stages are free for the epilogue
+
+    // the next tile's first slice goes into stage 1 now, so its latency hides
+    // under this tile's epilogue
+    pf = false;
+    {
+      const int t2 = tile + G;
+      if (t2 < total) {
+        const int e2 = t2 / per_expert;
+        const int rem2 = t2 - e2 * per_expert;
+        const int mt2 = rem2 / NTL, nt2 = rem2 - mt2 * NTL;
+        const int cnt2 = uniform(cnt_s[e2]);
+        if (cnt2 > 0) {
+          const int64_t base2 = int64_t(uniform(off_s[e2]));
+          const int rows = min(BK, cnt2);
+          const i32x4 ra2 = make_rsrc(g.a + base2 * M, uint32_t(rows) * uint32_t(M) * 2u);
+          const i32x4 rb2 = make_rsrc(g.b + base2 * N, uint32_t(rows) * uint32_t(N) * 2u);
+          const uint32_t sbase = lds0 + STAGE;
+#pragma unroll
+          for (int i = 0; i < A_LOADS; ++i) {
+            const int kr = (wid + kWaves * i) * A_RPL + lane / A_CPR;
+            const int lc = wg_swz(lane % A_CPR, kr);
+            dma16(ra2, (uint32_t(kr) * uint32_t(M) + uint32_t(mt2 * BM + 8 * lc)) * 2u,
+                  sbase + (wid + kWaves * i) * 1024);
+          }
+#pragma unroll
+          for (int i = 0; i < B_LOADS; ++i) {
+            const int kr = (wid + kWaves * i) * B_RPL + lane / B_CPR;
+            const int lc = wg_swz(lane % B_CPR, kr);
+            dma16(rb2, (uint32_t(kr) * uint32_t(N) + uint32_t(nt2 * BN + 8 * lc)) * 2u,
+                  sbase + A_BYTES + (wid + kWaves * i) * 1024);
+          }
+          pf = true;
+        }
+      }
+    }
 
     // epilogue, one pass per wavefront column: bf16 tile [BM, WCOL] in LDS,
     // then 16-byte row stores into dW1 / dW3 (or dW2)

@@ -154,7 +154,6 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
   constexpr int A_LOADS = A_BYTES / 1024 / kWaves, B_LOADS = B_BYTES / 1024 / kWaves;
   constexpr int CPR = BK / 8;           // 16-byte chunks per staged row
   constexpr int RB = 64 / CPR;          // rows per 1 KiB wave-load
-  constexpr int WAIT = (STAGES - 2) * (A_LOADS + B_LOADS);
   static_assert(WAVES_M * WROWS == BM && WAVES_M * WAVES_N == kWaves, "wavefront grid");
   static_assert(A_LOADS * 1024 * kWaves == A_BYTES && B_LOADS * 1024 * kWaves == B_BYTES,
                 "whole 1 KiB wave-loads");
@@ -297,23 +296,27 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
       const int r = (wid + kWaves * i) * RB + ld_r;  // gated: first half gate rows, then up
       ob[i] = (uint32_t(GATED ? r % (BN / 2) : r) * b_row + ld_ch * 8) * 2u;
     }
-    auto issue = [&](int kt, int st) {
-      const uint32_t sbase = lds0 + st * STAGE;
+    // SM: a tile of at most 64 rows, staged with 64-row A slices so that
+    // three stages fit where the full tile has two
+    auto issue = [&](int kt, int st, auto sm_tag) {
+      constexpr bool SM = decltype(sm_tag)::value;
+      constexpr int AB = SM ? 64 * BK * 2 : A_BYTES, ST = AB + B_BYTES, AL = AB / 1024 / kWaves;
+      const uint32_t sbase = lds0 + st * ST;
       const uint32_t k0 = uint32_t(kt) * BK;
 #pragma unroll
-      for (int i = 0; i < A_LOADS; ++i) dma16(ra, oa[i], k0 * 2, sbase + (wid + kWaves * i) * 1024);
+      for (int i = 0; i < AL; ++i) dma16(ra, oa[i], k0 * 2, sbase + (wid + kWaves * i) * 1024);
       if constexpr (KIND == kKSplit) {
         // the same slice of b0 or, past k_split, of b1 (slices never straddle it)
         const bool second = k0 >= uint32_t(g.k_split);
         const uint32_t kb = second ? k0 - uint32_t(g.k_split) : k0;
 #pragma unroll
         for (int i = 0; i < B_LOADS; ++i)
-          dma16(second ? rb1 : rb0, ob[i], kb * 2, sbase + A_BYTES + (wid + kWaves * i) * 1024);
+          dma16(second ? rb1 : rb0, ob[i], kb * 2, sbase + AB + (wid + kWaves * i) * 1024);
       } else {
 #pragma unroll
         for (int i = 0; i < B_LOADS; ++i)
           dma16((GATED && i >= B_LOADS / 2) ? rb1 : rb0, ob[i], uint32_t(kt) * b_step * 2,
-                sbase + A_BYTES + (wid + kWaves * i) * 1024);
+                sbase + AB + (wid + kWaves * i) * 1024);
       }
     };
 
@@ -335,8 +338,13 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
     // 16-wide step are read before the barrier, so those MFMAs run while the
     // first reads of the next slice are in flight. Every variant executes the
     // same loads and barriers; only the matrix work differs.
-    auto kloop = [&](auto nb_tag) {
+    auto kloop = [&](auto nb_tag, auto sm_tag) {
       constexpr int NB = decltype(nb_tag)::value;
+      constexpr bool SM = decltype(sm_tag)::value;
+      constexpr int AB = SM ? 64 * BK * 2 : A_BYTES, ST = AB + B_BYTES;
+      constexpr int NS = SM ? 3 : STAGES, AL = AB / 1024 / kWaves;
+      constexpr int WT = (NS - 2) * (AL + B_LOADS);
+      static_assert(NS * ST <= STAGES * STAGE, "small-tile stages fit");
       bf16x8 fa[2][TM], fb[2][TN];
       auto read_frags = [&](const char* base, int kk, bf16x8 (&a)[TM], bf16x8 (&b)[TN]) {
         const int ch = 2 * kk + (lane >> 5);
@@ -346,7 +354,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
         for (int j = 0; j < TN; ++j) {
           const int brow = GATED ? (j / HALF) * (BN / 2) + wn * WCOL + (j % HALF) * 32
                                  : wn * WCOL + j * 32;
-          b[j] = *reinterpret_cast<const bf16x8*>(base + A_BYTES +
+          b[j] = *reinterpret_cast<const bf16x8*>(base + AB +
                                                   swz<BK>(brow + (lane & 31), ch));
         }
 #pragma unroll
@@ -363,14 +371,14 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
       };
 
 #pragma unroll
-      for (int s = 0; s < STAGES - 1; ++s)
-        if (s < KT) issue(s, s);
-      if (STAGES - 2 < KT) wait_vmcnt<WAIT>(); else wait_vmcnt<0>();
+      for (int s = 0; s < NS - 1; ++s)
+        if (s < KT) issue(s, s, sm_tag);
+      if (NS - 2 < KT) wait_vmcnt<WT>(); else wait_vmcnt<0>();
       __syncthreads();  // slice 0 visible
-      if (STAGES - 1 < KT) issue(STAGES - 1, STAGES - 1);
+      if (NS - 1 < KT) issue(NS - 1, NS - 1, sm_tag);
       read_frags(smem, 0, fa[0], fb[0]);
       for (int kt = 0; kt < KT; ++kt) {
-        const char* base = smem + (kt % STAGES) * STAGE;
+        const char* base = smem + (kt % NS) * ST;
 #pragma unroll
         for (int kk = 0; kk + 1 < KK; ++kk) {
           read_frags(base, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
@@ -380,17 +388,23 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
         }
         if (kt + 1 < KT) {
           // slice kt+1 landed (this wavefront's part), and all of slice kt is read
-          if (kt + STAGES - 1 < KT) wait_vmcnt<WAIT>(); else wait_vmcnt<0>();
+          if (kt + NS - 1 < KT) wait_vmcnt<WT>(); else wait_vmcnt<0>();
           __syncthreads();
-          if (kt + STAGES < KT) issue(kt + STAGES, (kt + STAGES) % STAGES);
-          read_frags(smem + ((kt + 1) % STAGES) * STAGE, 0, fa[0], fb[0]);
+          if (kt + NS < KT) issue(kt + NS, (kt + NS) % NS, sm_tag);
+          read_frags(smem + ((kt + 1) % NS) * ST, 0, fa[0], fb[0]);
         }
         mfma(fa[(KK - 1) & 1], fb[(KK - 1) & 1]);
       }
     };
     // one K-loop copy per block count 0..TM: a wavefront multiplies only the
-    // blocks that hold rows
-    with_block_count<TM>(nblk, kloop);
+    // blocks that hold rows. A forward tile of at most 64 rows (the few rows
+    // of a lightly routed expert) is bound by load latency, not by its matrix
+    // work: it gets the three-stage layout
+    constexpr bool SMALL_OK = (KIND == kGated || KIND == kPlain) && TM >= 2;
+    if (SMALL_OK && rows_valid <= 64)
+      with_block_count<(TM >= 2 ? 2 : TM)>(nblk, [&](auto nb) { kloop(nb, std::bool_constant<SMALL_OK>{}); });
+    else
+      with_block_count<TM>(nblk, [&](auto nb) { kloop(nb, std::false_type{}); });
     __syncthreads();  // every wavefront is done reading the last slice
 
     // accumulators (lane: column lane % 32, rows 8*(q/4) + 4*(lane/32) + q%4)

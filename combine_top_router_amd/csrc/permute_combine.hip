@@ -155,44 +155,61 @@ __global__ __launch_bounds__(256) void combine_kernel(const u32x4* __restrict__ 
   if (t >= T) return;
   const int lane = lane_id();
 
+  // the token's local slots, in slot order (wave-uniform: scalar registers)
   int64_t rows[KM];
   float w[KM];
+  int nv = 0;
 #pragma unroll
   for (int j = 0; j < KM; ++j) {
     if (j < k) {
       const int r = dst_row[t * k + j];
-      rows[j] = (r >= 0 && r < y_rows) ? int64_t(r) : -1;
-      w[j] = topk_w ? topk_w[t * k + j] : 1.0f;  // no weights: a plain sum
-    } else {
-      rows[j] = -1;
-      w[j] = 0.f;
+      if (r >= 0 && r < y_rows) {
+        rows[nv] = int64_t(r);
+        w[nv] = topk_w ? topk_w[t * k + j] : 1.0f;  // no weights: a plain sum
+        ++nv;
+      }
     }
   }
 
+  // kU vectors per lane per round, all of a slot's loads issued before its
+  // products, so a wavefront keeps kU KiB per slot in flight
+  constexpr int kU = 4;
   u32x4* dst = out + t * hv;
-  for (int v = lane; v < hv; v += kWave) {
-    u32x4 in[KM];
+  for (int v0 = lane; v0 < hv; v0 += kU * kWave) {
+    float acc[kU][NV];
 #pragma unroll
-    for (int j = 0; j < KM; ++j)
-      if (rows[j] >= 0) in[j] = __builtin_nontemporal_load(y + rows[j] * hv + v);
-    float acc[NV];
+    for (int u = 0; u < kU; ++u)
 #pragma unroll
-    for (int q = 0; q < NV; ++q) acc[q] = 0.f;
+      for (int q = 0; q < NV; ++q) acc[u][q] = 0.f;
+    for (int j = 0; j < nv; ++j) {
+      u32x4 in[kU];
+      const u32x4* src = y + rows[j] * hv;
 #pragma unroll
-    for (int j = 0; j < KM; ++j) {
-      if (rows[j] < 0) continue;
-      float f[NV];
-      R::load(in[j], f);
+      for (int u = 0; u < kU; ++u)
+        if (v0 + u * kWave < hv) in[u] = __builtin_nontemporal_load(src + v0 + u * kWave);
 #pragma unroll
-      for (int q = 0; q < NV; ++q) acc[q] = acc[q] + w[j] * f[q];
+      for (int u = 0; u < kU; ++u) {
+        if (v0 + u * kWave < hv) {
+          float f[NV];
+          R::load(in[u], f);
+#pragma unroll
+          for (int q = 0; q < NV; ++q) acc[u][q] = acc[u][q] + w[j] * f[q];
+        }
+      }
     }
-    if (shared) {  // the shared expert's row joins before the one rounding
-      float f[NV];
-      R::load(__builtin_nontemporal_load(shared + t * hv + v), f);
 #pragma unroll
-      for (int q = 0; q < NV; ++q) acc[q] = acc[q] + f[q];
+    for (int u = 0; u < kU; ++u) {
+      const int v = v0 + u * kWave;
+      if (v < hv) {
+        if (shared) {  // the shared expert's row joins before the one rounding
+          float f[NV];
+          R::load(__builtin_nontemporal_load(shared + t * hv + v), f);
+#pragma unroll
+          for (int q = 0; q < NV; ++q) acc[u][q] = acc[u][q] + f[q];
+        }
+        __builtin_nontemporal_store(R::store(acc[u]), dst + v);
+      }
     }
-    __builtin_nontemporal_store(R::store(acc), dst + v);
   }
 }
 

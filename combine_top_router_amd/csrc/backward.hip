@@ -68,21 +68,38 @@ __global__ __launch_bounds__(256) void combine_backward_kernel(
 #pragma unroll
     for (int q = 0; q < 8; ++q) dot[j][q] = 0.f;
 
+  // kU vectors per lane per round (ascending, so each lane's partial sums
+  // take the row in the same order as one vector at a time), each slot's
+  // loads issued together before its products
+  constexpr int kU = 4;
   const u32x4* g_row = grad_out + t * hv;
-  for (int v = lane; v < hv; v += kWave) {
-    float g[8];
-    unpack8(__builtin_nontemporal_load(g_row + v), g);
+  for (int v0 = lane; v0 < hv; v0 += kU * kWave) {
+    u32x4 graw[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+      if (v0 + u * kWave < hv) graw[u] = __builtin_nontemporal_load(g_row + v0 + u * kWave);
 #pragma unroll
     for (int j = 0; j < KM; ++j) {
       if (rows[j] < 0) continue;
-      float yv[8], gy[8];
-      unpack8(__builtin_nontemporal_load(y + rows[j] * hv + v), yv);
+      u32x4 yraw[kU];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        dot[j][q] = dot[j][q] + g[q] * yv[q];
-        gy[q] = w[j] * g[q];
+      for (int u = 0; u < kU; ++u)
+        if (v0 + u * kWave < hv) yraw[u] = __builtin_nontemporal_load(y + rows[j] * hv + v0 + u * kWave);
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int v = v0 + u * kWave;
+        if (v < hv) {
+          float g[8], yv[8], gy[8];
+          unpack8(graw[u], g);
+          unpack8(yraw[u], yv);
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            dot[j][q] = dot[j][q] + g[q] * yv[q];
+            gy[q] = w[j] * g[q];
+          }
+          __builtin_nontemporal_store(pack8(gy), grad_y + rows[j] * hv + v);
+        }
       }
-      __builtin_nontemporal_store(pack8(gy), grad_y + rows[j] * hv + v);
     }
   }
 

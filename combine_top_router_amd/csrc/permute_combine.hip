@@ -41,24 +41,30 @@ __global__ __launch_bounds__(256) void permute_kernel(const u32x4* __restrict__ 
   const int lane = lane_id();
 
   int64_t rows[16];
+  float wts[16];  // read with the rows, ahead of the row loads
   int nvalid = 0;
 #pragma unroll
   for (int j = 0; j < (K > 0 ? K : 16); ++j) {
     if (j < k) {
       const int r = dst_row[t * k + j];
       rows[j] = (r >= 0 && r < m_cap) ? int64_t(r) : -1;
+      wts[j] = WEIGHTED ? topk_w[t * k + j] : 1.0f;
       nvalid += rows[j] >= 0;
     } else {
       rows[j] = -1;
+      wts[j] = 0.f;
     }
   }
   if (nvalid == 0) return;  // no local slot: this token's row is not read at all
 
+  // vectors per lane per pass: the weighted copy's conversions need registers,
+  // so it buffers fewer and keeps more wavefronts resident
+  constexpr int NB = WEIGHTED ? kBuf / 2 : kBuf;
   const u32x4* src = x + t * hv;
-  for (int base = 0; base < hv; base += kBuf * kWave) {
-    u32x4 buf[kBuf];
+  for (int base = 0; base < hv; base += NB * kWave) {
+    u32x4 buf[NB];
 #pragma unroll
-    for (int i = 0; i < kBuf; ++i) {
+    for (int i = 0; i < NB; ++i) {
       const int v = base + i * kWave + lane;
       if (v < hv) buf[i] = __builtin_nontemporal_load(src + v);
     }
@@ -67,9 +73,9 @@ __global__ __launch_bounds__(256) void permute_kernel(const u32x4* __restrict__ 
       if (j >= k || rows[j] < 0) continue;
       u32x4* dst = x_perm + rows[j] * hv;
       if constexpr (WEIGHTED) {
-        const float w = topk_w[t * k + j];
+        const float w = wts[j];
 #pragma unroll
-        for (int i = 0; i < kBuf; ++i) {
+        for (int i = 0; i < NB; ++i) {
           const int v = base + i * kWave + lane;
           if (v < hv) {
             float f[8];
@@ -81,7 +87,7 @@ __global__ __launch_bounds__(256) void permute_kernel(const u32x4* __restrict__ 
         }
       } else {
 #pragma unroll
-        for (int i = 0; i < kBuf; ++i) {
+        for (int i = 0; i < NB; ++i) {
           const int v = base + i * kWave + lane;
           if (v < hv) dst[v] = buf[i];
         }

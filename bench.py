@@ -93,10 +93,23 @@ def roof_entry(ms: float, bound: str, amount) -> dict:
     return out
 
 
+def source_hash(path: str) -> str:
+    """First 16 hex digits of the sha256 of a source file's code: comment-only
+    and blank lines are dropped and trailing comments stripped, so a comment
+    edit keeps counters taken on the same code valid."""
+    import hashlib
+    import re
+    lines = []
+    for line in open(path, encoding="utf-8"):
+        code = re.sub(r"//.*$", "", line).rstrip()
+        if code.strip():
+            lines.append(code)
+    return hashlib.sha256("\n".join(lines).encode()).hexdigest()[:16]
+
+
 def traffic_record(kernel: str, workload: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it was
     taken on the current kernel source (else None)."""
-    import hashlib
     path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_counters.md")
     src = os.path.join(ROOT, "combine_top_router_amd", "csrc", "grouped_gemm.hip")
     if not os.path.exists(path):
@@ -106,8 +119,7 @@ def traffic_record(kernel: str, workload: str):
         if line.startswith("- ") and ":" in line:
             k, v = line[2:].split(":", 1)
             rec[k.strip()] = v.strip().strip("`")
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
-    if rec.get("source_sha256_16") != sha or "hbm_bytes_per_launch" not in rec:
+    if rec.get("source_sha256_16") != source_hash(src) or "hbm_bytes_per_launch" not in rec:
         return None
     return float(rec["hbm_bytes_per_launch"])
 

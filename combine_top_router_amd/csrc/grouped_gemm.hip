@@ -17,8 +17,8 @@
 //  * v_mfma_f32_32x32x16_bf16: a wavefront multiplies a 32x16 A slice by a
 //    16x32 B slice into 32x32 fp32 accumulators; each lane feeds 8
 //    consecutive K values of one row of A and one row of B^T, so both
-//    operands are read K-contiguous (weights are stored output-major,
-//    [E, N, K], by the one-time repack).
+//    operands are read K-contiguous (forward weights are repacked once,
+//    output-major and cut into K-slices that are each one contiguous run).
 //  * 8 wavefronts per workgroup (2 per SIMD), each owning TM 32-row blocks
 //    of accumulators. The main tile is 320 rows x 256 staged B rows, waves 2
 //    (rows) x 4 (columns), 160 rows x 64 B rows each: 160 accumulator VGPRs,
@@ -33,7 +33,12 @@
 //    is in flight while the matrix cores consume slice kt, one barrier per
 //    slice. Each lane picks the global chunk that belongs at its LDS slot,
 //    which realises an XOR swizzle of the 16-byte chunks within a row so the
-//    fragment reads spread over the LDS banks.
+//    fragment reads spread over the LDS banks. A lane's offsets stay fixed
+//    for the tile and the K-slice advance rides in the scalar offset. A tile
+//    of at most 64 rows (forward kinds) stages 64-row A slices in three
+//    stages instead.
+//  * The next 16-wide step's fragment reads are interleaved with the current
+//    step's MFMAs (scheduling hints), B fragments first.
 //  * Ragged groups: each workgroup derives the per-expert m-tile prefix from
 //    the device-side counts (no host sync; grid sized for the chip, not for
 //    the routing), then walks tile ids persistently. Ids run expert-major,
@@ -48,7 +53,9 @@
 //    read as zeros through the buffer bound (their results are never stored).
 //  * Epilogue through LDS: fp32 -> bf16 (SwiGLU for the gated pair) into a
 //    [BM, OUT_N] tile, then 16-byte row-contiguous stores of the valid rows;
-//    a tile larger than the stage buffers goes out in two column passes.
+//    a tile larger than the stage buffers goes out in two column passes. The
+//    down backward stages its fp32 dh per wavefront column and finishes the
+//    SwiGLU backward row-contiguously (16-byte loads of g, u and stores).
 #include <algorithm>
 #include <type_traits>
 #include <utility>

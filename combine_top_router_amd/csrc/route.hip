@@ -12,9 +12,9 @@
 // tokens at once; lane j of the group holds the VPL consecutive logits of
 // experts j*VPL .. j*VPL+VPL-1 (one contiguous load per lane) as 64-bit keys
 // whose order is (logit descending, id ascending). Each of the k rounds takes
-// the lane's best key, a log2(G)-step xor-shuffle max inside the group, and
-// retires the winner; lane j keeps the j-th winner. HBM-bound: T*E*4 bytes
-// in, T*k*8 out.
+// the lane's best key, a max inside the group (DPP exchanges within the
+// group's 16-lane row), and retires the winner; lane j keeps the j-th winner.
+// T*E*4 bytes in, T*k*8 out.
 #include "moe_internal.h"
 
 namespace moe {
@@ -39,15 +39,37 @@ __device__ __forceinline__ uint64_t make_key(float f, int e) {
   return (static_cast<uint64_t>(ordered_bits(f)) << 32) | static_cast<uint32_t>(~e);
 }
 
+// 64-bit value of another lane of the same 16-lane DPP row (CTRL: a DPP
+// row pattern), as two 32-bit DPP moves.
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp64(uint64_t v) {
+  const uint32_t lo = __builtin_amdgcn_update_dpp(0u, static_cast<uint32_t>(v), CTRL, 0xF, 0xF, false);
+  const uint32_t hi = __builtin_amdgcn_update_dpp(0u, static_cast<uint32_t>(v >> 32), CTRL, 0xF, 0xF, false);
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+// Max over the G lanes of a group, in every lane of the group. Inside a
+// 16-lane row the exchanges are DPP moves (rotate by 8 and 4 for 16-lane
+// groups, the half-row mirror for 8-lane groups, then two quad swaps); a
+// 32-lane group first combines its two rows through a shuffle. Any pairing
+// gives the same maximum.
 template <int G>
 __device__ __forceinline__ uint64_t group_max_u64(uint64_t v) {
-#pragma unroll
-  for (int off = G / 2; off >= 1; off >>= 1) {
-    const uint32_t lo = __shfl_xor(static_cast<uint32_t>(v), off, kWave);
-    const uint32_t hi = __shfl_xor(static_cast<uint32_t>(v >> 32), off, kWave);
-    const uint64_t o = (static_cast<uint64_t>(hi) << 32) | lo;
-    v = o > v ? o : v;
+  auto mx = [](uint64_t a, uint64_t b) { return a > b ? a : b; };
+  if constexpr (G == 32) {
+    const uint32_t lo = __shfl_xor(static_cast<uint32_t>(v), 16, kWave);
+    const uint32_t hi = __shfl_xor(static_cast<uint32_t>(v >> 32), 16, kWave);
+    v = mx(v, (static_cast<uint64_t>(hi) << 32) | lo);
   }
+  if constexpr (G >= 16) {
+    v = mx(v, dpp64<0x128>(v));  // row_ror:8
+    v = mx(v, dpp64<0x124>(v));  // row_ror:4
+  } else {
+    static_assert(G == 8, "groups of 8, 16 or 32 lanes");
+    v = mx(v, dpp64<0x141>(v));  // row_half_mirror
+  }
+  v = mx(v, dpp64<0x4E>(v));  // quad_perm [2,3,0,1]
+  v = mx(v, dpp64<0xB1>(v));  // quad_perm [1,0,3,2]
   return v;
 }
 

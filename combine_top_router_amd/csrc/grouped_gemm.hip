@@ -37,6 +37,11 @@
 //    for the tile and the K-slice advance rides in the scalar offset. A tile
 //    of at most 64 rows (forward kinds) stages 64-row A slices in three
 //    stages instead.
+//  * With two stages, a slice's loads go out one per MFMA of the step that
+//    follows the barrier (weights first, then activations) rather than back
+//    to back: all eight wavefronts issuing theirs at once overfill the
+//    texture unit's command queue, and a wavefront stalled on a load issue
+//    stalls its MFMAs too.
 //  * The next 16-wide step's fragment reads are interleaved with the current
 //    step's MFMAs (scheduling hints), B fragments first.
 //  * Ragged groups: each workgroup derives the per-expert m-tile prefix from
@@ -132,6 +137,12 @@ __device__ __forceinline__ void interleave_slot() {
 template <int NR, int NM, int... T>
 __device__ __forceinline__ void interleave_reads(std::integer_sequence<int, T...>) {
   (interleave_slot<T, NR, NM>(), ...);
+}
+
+// f(std::integral_constant<int, q>) for q = 0, 1, ..., in order.
+template <class F, int... Q>
+__device__ __forceinline__ void for_each_index(F&& f, std::integer_sequence<int, Q...>) {
+  (f(std::integral_constant<int, Q>{}), ...);
 }
 
 // Calls f(std::integral_constant<int, nb>) for the run-time nb in 0..NB, so
@@ -303,28 +314,33 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
       const int r = (wid + kWaves * i) * RB + ld_r;  // gated: first half gate rows, then up
       ob[i] = (uint32_t(GATED ? r % (BN / 2) : r) * b_row + ld_ch * 8) * 2u;
     }
-    // SM: a tile of at most 64 rows, staged with 64-row A slices so that
-    // three stages fit where the full tile has two
+    // wave-load i of K-slice kt: A rows into the stage's A part at LDS byte
+    // a_lds, B rows into its B part at b_lds
+    auto load_a = [&](int i, int kt, uint32_t a_lds) {
+      dma16(ra, oa[i], uint32_t(kt) * BK * 2, a_lds + (wid + kWaves * i) * 1024);
+    };
+    auto load_b = [&](int i, int kt, uint32_t b_lds) {
+      if constexpr (KIND == kKSplit) {
+        // the same slice of b0 or, past k_split, of b1 (slices never straddle it)
+        const uint32_t k0 = uint32_t(kt) * BK;
+        const bool second = k0 >= uint32_t(g.k_split);
+        dma16(second ? rb1 : rb0, ob[i], (second ? k0 - uint32_t(g.k_split) : k0) * 2,
+              b_lds + (wid + kWaves * i) * 1024);
+      } else {
+        dma16((GATED && i >= B_LOADS / 2) ? rb1 : rb0, ob[i], uint32_t(kt) * b_step * 2,
+              b_lds + (wid + kWaves * i) * 1024);
+      }
+    };
+    // all of slice kt into stage st. SM: a tile of at most 64 rows, staged
+    // with 64-row A slices so that three stages fit where the full tile has two
     auto issue = [&](int kt, int st, auto sm_tag) {
       constexpr bool SM = decltype(sm_tag)::value;
       constexpr int AB = SM ? 64 * BK * 2 : A_BYTES, ST = AB + B_BYTES, AL = AB / 1024 / kWaves;
       const uint32_t sbase = lds0 + st * ST;
-      const uint32_t k0 = uint32_t(kt) * BK;
 #pragma unroll
-      for (int i = 0; i < AL; ++i) dma16(ra, oa[i], k0 * 2, sbase + (wid + kWaves * i) * 1024);
-      if constexpr (KIND == kKSplit) {
-        // the same slice of b0 or, past k_split, of b1 (slices never straddle it)
-        const bool second = k0 >= uint32_t(g.k_split);
-        const uint32_t kb = second ? k0 - uint32_t(g.k_split) : k0;
+      for (int i = 0; i < AL; ++i) load_a(i, kt, sbase);
 #pragma unroll
-        for (int i = 0; i < B_LOADS; ++i)
-          dma16(second ? rb1 : rb0, ob[i], kb * 2, sbase + AB + (wid + kWaves * i) * 1024);
-      } else {
-#pragma unroll
-        for (int i = 0; i < B_LOADS; ++i)
-          dma16((GATED && i >= B_LOADS / 2) ? rb1 : rb0, ob[i], uint32_t(kt) * b_step * 2,
-                sbase + AB + (wid + kWaves * i) * 1024);
-      }
+      for (int i = 0; i < B_LOADS; ++i) load_b(i, kt, sbase + AB);
     };
 
     f32x16 acc[TM][TN];
@@ -376,6 +392,38 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
           for (int j = 0; j < TN; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
       };
+      auto steps = [&](const char* base) {
+#pragma unroll
+        for (int kk = 0; kk + 1 < KK; ++kk) {
+          read_frags(base, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
+          mfma(fa[kk & 1], fb[kk & 1]);
+          // interleave the next step's fragment reads with this step's products
+          if constexpr (NB > 0) interleave_reads<NB + TN, NB * TN>(std::make_integer_sequence<int, NB + TN>{});
+        }
+      };
+      // A step's products with the loads of slice kt2 between them: product q,
+      // then load q, the loads left over after the last product. B loads come
+      // first (the weights stream from memory, so they get the longest lead),
+      // then A. A load issues only once the matrix pipe has taken the product
+      // before it, so each wavefront's loads go out spread over its products;
+      // issued back to back after the barrier, every wavefront's loads at once
+      // fill the texture unit's command queue and stall the issuing
+      // wavefronts, products included. ld false: the products alone.
+      constexpr int NL = AL + B_LOADS, NP = NB * TN, NQ = NP > NL ? NP : NL;
+      auto mfma_loads = [&](const bf16x8 (&a)[TM], const bf16x8 (&b)[TN], int kt2, bool ld) {
+        const uint32_t sbase = lds0 + (kt2 % NS) * ST;
+        for_each_index([&](auto q_tag) {
+          constexpr int q = decltype(q_tag)::value;
+          if constexpr (q < NP)
+            acc[q / TN][q % TN] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                a[q / TN], b[q % TN], acc[q / TN][q % TN], 0, 0, 0);
+          if constexpr (q < B_LOADS) {
+            if (ld) load_b(q, kt2, sbase + AB);
+          } else if constexpr (q < NL) {
+            if (ld) load_a(q - B_LOADS, kt2, sbase);
+          }
+        }, std::make_integer_sequence<int, NQ>{});
+      };
 
 #pragma unroll
       for (int s = 0; s < NS - 1; ++s)
@@ -384,15 +432,24 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
       __syncthreads();  // slice 0 visible
       if (NS - 1 < KT) issue(NS - 1, NS - 1, sm_tag);
       read_frags(smem, 0, fa[0], fb[0]);
-      for (int kt = 0; kt < KT; ++kt) {
-        const char* base = smem + (kt % NS) * ST;
-#pragma unroll
-        for (int kk = 0; kk + 1 < KK; ++kk) {
-          read_frags(base, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
-          mfma(fa[kk & 1], fb[kk & 1]);
-          // interleave the next step's fragment reads with this step's products
-          if constexpr (NB > 0) interleave_reads<NB + TN, NB * TN>(std::make_integer_sequence<int, NB + TN>{});
+      if constexpr (!SM && NS == 2) {
+        // Two stages: the barrier after slice kt's steps releases slice kt's
+        // stage, and slice kt+2's loads into it ride with slice kt's last-step
+        // products. The last slice is peeled so that the loop has one path.
+        for (int kt = 0; kt + 1 < KT; ++kt) {
+          steps(smem + (kt % NS) * ST);
+          // slice kt+1 landed (this wavefront's part), and all of slice kt is read
+          wait_vmcnt<0>();
+          __syncthreads();
+          read_frags(smem + ((kt + 1) % NS) * ST, 0, fa[0], fb[0]);
+          mfma_loads(fa[(KK - 1) & 1], fb[(KK - 1) & 1], kt + NS, kt + NS < KT);
         }
+        steps(smem + ((KT - 1) % NS) * ST);
+        mfma(fa[(KK - 1) & 1], fb[(KK - 1) & 1]);
+        return;
+      }
+      for (int kt = 0; kt < KT; ++kt) {
+        steps(smem + (kt % NS) * ST);
         if (kt + 1 < KT) {
           // slice kt+1 landed (this wavefront's part), and all of slice kt is read
           if (kt + NS - 1 < KT) wait_vmcnt<WT>(); else wait_vmcnt<0>();

@@ -139,11 +139,6 @@ __device__ __forceinline__ void interleave_reads(std::integer_sequence<int, T...
   (interleave_slot<T, NR, NM>(), ...);
 }
 
-// f(std::integral_constant<int, q>) for q = 0, 1, ..., in order.
-template <class F, int... Q>
-__device__ __forceinline__ void for_each_index(F&& f, std::integer_sequence<int, Q...>) {
-  (f(std::integral_constant<int, Q>{}), ...);
-}
 
 // Calls f(std::integral_constant<int, nb>) for the run-time nb in 0..NB, so
 // each block count gets its own fully unrolled copy of f.

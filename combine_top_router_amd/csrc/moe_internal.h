@@ -4,6 +4,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <utility>
+
 namespace moe {
 
 constexpr int kWave = 64;
@@ -104,6 +107,13 @@ __device__ __forceinline__ int64_t uniform(int64_t v) {
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// f(std::integral_constant<int, q>) for q = 0, 1, ..., in order: a fully
+// unrolled sequence whose steps can differ at compile time.
+template <class F, int... Q>
+__device__ __forceinline__ void for_each_index(F&& f, std::integer_sequence<int, Q...>) {
+  (f(std::integral_constant<int, Q>{}), ...);
+}
 
 }  // namespace moe
 

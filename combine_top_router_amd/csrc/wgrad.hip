@@ -121,17 +121,22 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(WgradArgs g) {
       const int lc = wg_swz(lane % B_CPR, kr);
       ob[i] = (uint32_t(kr) * uint32_t(N) + uint32_t(n0 + 8 * lc)) * 2u;
     }
+    // the buffer ranges of slice kt end at the expert's last row (none past it)
+    auto slice_rsrc = [&](int kt, i32x4& ra, i32x4& rb) {
+      const int rows = max(0, min(BK, cnt - kt * BK));
+      ra = make_rsrc(g.a + (base + int64_t(kt) * BK) * M, uint32_t(rows) * uint32_t(M) * 2u);
+      rb = make_rsrc(g.b + (base + int64_t(kt) * BK) * N, uint32_t(rows) * uint32_t(N) * 2u);
+    };
+    // wave-load q of a slice (A loads first, then B) into the stage at sbase
+    auto load = [&](int q, const i32x4& ra, const i32x4& rb, uint32_t sbase) {
+      if (q < A_LOADS) dma16(ra, oa[q], sbase + (wid + kWaves * q) * 1024);
+      else dma16(rb, ob[q - A_LOADS], sbase + A_BYTES + (wid + kWaves * (q - A_LOADS)) * 1024);
+    };
     auto issue = [&](int kt, int st) {
-      // the slice's buffer ranges end at the expert's last row
-      const int rows = min(BK, cnt - kt * BK);
-      const i32x4 ra = make_rsrc(g.a + (base + int64_t(kt) * BK) * M, uint32_t(rows) * uint32_t(M) * 2u);
-      const i32x4 rb = make_rsrc(g.b + (base + int64_t(kt) * BK) * N, uint32_t(rows) * uint32_t(N) * 2u);
-      const uint32_t sbase = lds0 + st * STAGE;
+      i32x4 ra, rb;
+      slice_rsrc(kt, ra, rb);
 #pragma unroll
-      for (int i = 0; i < A_LOADS; ++i) dma16(ra, oa[i], sbase + (wid + kWaves * i) * 1024);
-#pragma unroll
-      for (int i = 0; i < B_LOADS; ++i)
-        dma16(rb, ob[i], sbase + A_BYTES + (wid + kWaves * i) * 1024);
+      for (int q = 0; q < A_LOADS + B_LOADS; ++q) load(q, ra, rb, lds0 + st * STAGE);
     };
 
     f32x16 acc[TM][TN];
@@ -166,6 +171,26 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(WgradArgs g) {
         for (int j = 0; j < TN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
     };
+    // A step's products with slice kt2's loads between them (product q, then
+    // load q): issued back to back after the barrier, every wavefront's loads
+    // at once overfill the texture unit's command queue and stall the
+    // wavefronts, their products with them. ld false: the products alone.
+    constexpr int NL = A_LOADS + B_LOADS, NP = TM * TN, NQ = NP > NL ? NP : NL;
+    auto mfma_loads = [&](const bf16x8 (&fa)[TM], const bf16x8 (&fb)[TN], int kt2, int st2,
+                          bool ld) {
+      i32x4 ra, rb;
+      slice_rsrc(kt2, ra, rb);
+      const uint32_t sbase = lds0 + st2 * STAGE;
+      for_each_index([&](auto q_tag) {
+        constexpr int q = decltype(q_tag)::value;
+        if constexpr (q < NP)
+          acc[q / TN][q % TN] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              fa[q / TN], fb[q % TN], acc[q / TN][q % TN], 0, 0, 0);
+        if constexpr (q < NL) {
+          if (ld) load(q, ra, rb, sbase);
+        }
+      }, std::make_integer_sequence<int, NQ>{});
+    };
 
     const int sp = pf ? 1 : 0;  // stage of slice 0
     if (KT > 0) {
@@ -175,21 +200,25 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(WgradArgs g) {
       __syncthreads();  // slice 0 visible
       if (KT > 1) issue(1, (1 + sp) & 1);
       read_frags(smem + sp * STAGE, 0, fa[0], fb[0]);
-      for (int kt = 0; kt < KT; ++kt) {
-        const char* sb = smem + ((kt + sp) & 1) * STAGE;
+      auto steps = [&](const char* sb) {
 #pragma unroll
         for (int kk = 0; kk < 3; ++kk) {
           read_frags(sb, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
           mfma(fa[kk & 1], fb[kk & 1]);
         }
-        if (kt + 1 < KT) {
-          wait_vmcnt<0>();  // slice kt+1 landed (this wavefront's part)
-          __syncthreads();  // ... everyone's, and slice kt is read
-          if (kt + 2 < KT) issue(kt + 2, (kt + sp) & 1);
-          read_frags(smem + ((kt + 1 + sp) & 1) * STAGE, 0, fa[0], fb[0]);
-        }
-        mfma(fa[1], fb[1]);
+      };
+      // every slice but the last: its first three steps, the barrier, then its
+      // last step's products paced with slice kt+2's loads into the stage the
+      // barrier released; the last slice peeled so that the loop has one path
+      for (int kt = 0; kt + 1 < KT; ++kt) {
+        steps(smem + ((kt + sp) & 1) * STAGE);
+        wait_vmcnt<0>();  // slice kt+1 landed (this wavefront's part)
+        __syncthreads();  // ... everyone's, and slice kt is read
+        read_frags(smem + ((kt + 1 + sp) & 1) * STAGE, 0, fa[0], fb[0]);
+        mfma_loads(fa[1], fb[1], kt + 2, (kt + sp) & 1, kt + 2 < KT);
       }
+      steps(smem + ((KT - 1 + sp) & 1) * STAGE);
+      mfma(fa[1], fb[1]);
     }
     __syncthreads();  // the stages are free for the epilogue
 

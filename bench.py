@@ -93,25 +93,34 @@ def roof_entry(ms: float, bound: str, amount) -> dict:
     return out
 
 
-def source_hash(path: str) -> str:
-    """First 16 hex digits of the sha256 of a source file's code: comment-only
-    and blank lines are dropped and trailing comments stripped, so a comment
-    edit keeps counters taken on the same code valid."""
+# the sources a grouped-GEMM kernel is built from (its counters are tied to them)
+GEMM_SOURCES = ("grouped_gemm.hip", "moe_internal.h")
+
+
+def source_hash(*paths: str) -> str:
+    """First 16 hex digits of the sha256 of the source files' code, in order:
+    comment-only and blank lines are dropped and trailing comments stripped,
+    so a comment edit keeps counters taken on the same code valid."""
     import hashlib
     import re
     lines = []
-    for line in open(path, encoding="utf-8"):
-        code = re.sub(r"//.*$", "", line).rstrip()
-        if code.strip():
-            lines.append(code)
+    for path in paths:
+        for line in open(path, encoding="utf-8"):
+            code = re.sub(r"//.*$", "", line).rstrip()
+            if code.strip():
+                lines.append(code)
     return hashlib.sha256("\n".join(lines).encode()).hexdigest()[:16]
+
+
+def gemm_source_hash() -> str:
+    return source_hash(*(os.path.join(ROOT, "combine_top_router_amd", "csrc", f)
+                         for f in GEMM_SOURCES))
 
 
 def traffic_record(kernel: str, workload: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it was
     taken on the current kernel source (else None)."""
     path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_counters.md")
-    src = os.path.join(ROOT, "combine_top_router_amd", "csrc", "grouped_gemm.hip")
     if not os.path.exists(path):
         return None
     rec = {}
@@ -119,7 +128,7 @@ def traffic_record(kernel: str, workload: str):
         if line.startswith("- ") and ":" in line:
             k, v = line[2:].split(":", 1)
             rec[k.strip()] = v.strip().strip("`")
-    if rec.get("source_sha256_16") != source_hash(src) or "hbm_bytes_per_launch" not in rec:
+    if rec.get("source_sha256_16") != gemm_source_hash() or "hbm_bytes_per_launch" not in rec:
         return None
     return float(rec["hbm_bytes_per_launch"])
 

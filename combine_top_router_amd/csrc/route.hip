@@ -34,7 +34,9 @@ __device__ __forceinline__ float from_ordered(uint32_t o) {
 
 // Key: ordered logit in the high word, ~expert in the low word, so the max
 // key is the largest logit and, among equal logits, the lowest expert id.
-// 0 never occurs for a real expert (low word ~e != 0), so it marks "taken".
+// The low word is unique per expert and never 0, so 0 marks a slot with no
+// expert; a selected expert is retired by clearing its high word, which puts
+// it below every finite logit (whose ordered bits are at least 0x00800000).
 __device__ __forceinline__ uint64_t make_key(float f, int e) {
   return (static_cast<uint64_t>(ordered_bits(f)) << 32) | static_cast<uint32_t>(~e);
 }
@@ -110,8 +112,11 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
 #pragma unroll
     for (int v = 1; v < VPL; ++v) best = key[v] > best ? key[v] : best;
     best = group_max_u64<G>(best);
+    // retire the winner: the one key whose low word (its ~expert) matches
+    const uint32_t won = static_cast<uint32_t>(best);
 #pragma unroll
-    for (int v = 0; v < VPL; ++v) key[v] = key[v] == best ? 0ull : key[v];
+    for (int v = 0; v < VPL; ++v)
+      key[v] = static_cast<uint32_t>(key[v]) == won ? (key[v] & 0xffffffffull) : key[v];
     const float l = from_ordered(static_cast<uint32_t>(best >> 32));
     if (r == 0) l_max = l;
     if (j == r) {

@@ -47,9 +47,9 @@
 //  * Ragged groups: each workgroup derives the per-expert m-tile prefix from
 //    the device-side counts (no host sync; grid sized for the chip, not for
 //    the routing), then walks tile ids persistently. Ids run expert-major,
-//    then n-tile, then m-tile, and each of the 8 XCDs gets a contiguous range
-//    of ids, so the workgroups sharing a weight tile or an activation tile
-//    sit behind the same L2. An expert's c rows form ceil(c/BM) tiles of
+//    then over bands of 4 m-tiles, then n-tile, then m-tile within the band,
+//    and each of the 8 XCDs gets a contiguous range of ids, so the workgroups
+//    sharing a weight tile or an activation tile sit behind the same L2. An expert's c rows form ceil(c/BM) tiles of
 //    (nearly) equal height, so no tile is a short tail that would finish
 //    early and pull its workgroup out of step with the others sharing its
 //    data. Each wavefront runs a K loop specialised for the number of its
@@ -72,6 +72,7 @@ namespace {
 
 constexpr int kMaxExperts = 1024;
 constexpr int kWaves = 8;
+constexpr int kBand = 4;  // row tiles walked together (tile order, below)
 constexpr int kThreads = kWaves * kWave;
 
 // What a launch computes. The B operand holds, per local expert, N output
@@ -247,8 +248,23 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
     // tile coordinates are the same in every lane: keep them in scalar registers
     const int e = uniform(lo);
     const int mtiles = uniform(mt_prefix[e + 1] - mt_prefix[e]);
+    // Within the expert, row tiles go in bands of kBand, column tile major
+    // inside a band: the workgroups of one XCD (32 consecutive ids) then share
+    // the A slices of 4 row tiles and the B slices of 8 column tiles, instead
+    // of 32 row tiles and one column tile when an expert has many rows (each
+    // A tile would be fetched again for every column tile).
     const int rem = tile - uniform(mt_prefix[e]) * NT;
-    const int nt = rem / mtiles, mt = rem % mtiles;
+    const int full = mtiles / kBand * kBand;  // row tiles in whole bands
+    int nt, mt;
+    if (rem < full * NT) {
+      const int band = rem / (kBand * NT), r2 = rem % (kBand * NT);
+      nt = r2 / kBand;
+      mt = band * kBand + r2 % kBand;
+    } else {
+      const int tail = mtiles - full, r2 = rem - full * NT;
+      nt = r2 / tail;
+      mt = full + r2 % tail;
+    }
     // The expert's rows split into mtiles tiles of (nearly) equal height, a
     // multiple of 32 and at most BM: no short tail tile, so the workgroups that
     // share weight and activation tiles through L2 take about equally long and

@@ -83,6 +83,23 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(WgradArgs g) {
   const int wm = wid / WAVES_N, wn = wid % WAVES_N;
   const int M = g.m, N = g.n;
   const int MT = M / BM, NTL = N / BN, per_expert = MT * NTL;
+  // Output tiles of an expert in bands of kBand row tiles, column tile major
+  // inside a band: one XCD's 32 consecutive tiles then share the slices of 4
+  // row tiles and 8 column tiles instead of 1-2 row tiles and 16-28 column
+  // tiles. rem: tile index within the expert -> (row tile, column tile).
+  constexpr int kBand = 4;
+  const int full = MT / kBand * kBand;
+  auto coords = [&](int rem, int& mt, int& nt) {
+    if (rem < full * NTL) {
+      const int r2 = rem % (kBand * NTL);
+      nt = r2 / kBand;
+      mt = rem / (kBand * NTL) * kBand + r2 % kBand;
+    } else {
+      const int tail = MT - full, r2 = rem - full * NTL;
+      nt = r2 / tail;
+      mt = full + r2 % tail;
+    }
+  };
   for (int e = threadIdx.x; e < g.e_loc; e += kThreads) cnt_s[e] = g.counts[e], off_s[e] = g.offsets[e];
   __syncthreads();
   const int total = g.e_loc * per_expert;
@@ -100,8 +117,8 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(WgradArgs g) {
   bool pf = false;
   for (int tile = slot; tile < total; tile += G) {
     const int e = tile / per_expert;
-    const int rem = tile - e * per_expert;
-    const int mt = rem / NTL, nt = rem - mt * NTL;
+    int mt, nt;
+    coords(tile - e * per_expert, mt, nt);
     const int cnt = uniform(cnt_s[e]);
     const int64_t base = int64_t(uniform(off_s[e]));
     const int KT = (cnt + BK - 1) / BK;
@@ -229,8 +246,8 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(WgradArgs g) {
       const int t2 = tile + G;
       if (t2 < total) {
         const int e2 = t2 / per_expert;
-        const int rem2 = t2 - e2 * per_expert;
-        const int mt2 = rem2 / NTL, nt2 = rem2 - mt2 * NTL;
+        int mt2, nt2;
+        coords(t2 - e2 * per_expert, mt2, nt2);
         const int cnt2 = uniform(cnt_s[e2]);
         if (cnt2 > 0) {
           const int64_t base2 = int64_t(uniform(off_s[e2]));

@@ -73,25 +73,62 @@ __global__ __launch_bounds__(kTile) void dl_count_kernel(DlArgs a) {
   for (int e = tid; e < a.E; e += kTile) a.tile_expert[size_t(tile) * a.E + e] = hist[e];
 }
 
-// One workgroup: rank r's tile counts become exclusive bases (one thread per
-// rank walks the tiles in order), expert e's counts are summed.
+// Largest power of two <= n (n >= 1).
+__device__ __forceinline__ int pow2_floor(int n) { return 1 << (31 - __clz(n)); }
+
+// One workgroup: rank r's tile counts become exclusive bases over the tiles in
+// order, and expert e's tile counts are summed. Each rank (then each expert)
+// gets a group of P threads (a power of two, P * rows <= 1024), each thread a
+// contiguous run of tiles whose loads are independent; the run sums are then
+// scanned (ranks) or reduced (experts) across the group in LDS.
 __global__ __launch_bounds__(1024) void dl_scan_kernel(DlArgs a, int32_t* per_rank,
                                                       int32_t* per_expert) {
+  __shared__ int32_t part[1024];
   const int tid = threadIdx.x;
-  if (tid < a.ep) {
-    int run = 0;
-    for (int j = 0; j < a.tiles; ++j) {
-      int32_t* p = a.tile_rank + size_t(j) * a.ep + tid;
-      const int c = *p;
-      *p = run;
-      run += c;
+  {
+    const int P = pow2_floor(1024 / a.ep);
+    const int r = tid / P, p = tid % P;
+    const int C = (a.tiles + P - 1) / P;
+    const int j0 = min(a.tiles, p * C), j1 = min(a.tiles, j0 + C);
+    int sum = 0;
+    if (r < a.ep)
+      for (int j = j0; j < j1; ++j) sum += a.tile_rank[size_t(j) * a.ep + r];
+    part[tid] = sum;
+    __syncthreads();
+    // inclusive prefix of the run sums within each group (Hillis-Steele)
+    for (int off = 1; off < P; off <<= 1) {
+      const int v = p >= off ? part[tid - off] : 0;
+      __syncthreads();
+      part[tid] += v;
+      __syncthreads();
     }
-    per_rank[tid] = run;
+    if (r < a.ep) {
+      int run = part[tid] - sum;
+      for (int j = j0; j < j1; ++j) {
+        int32_t* q = a.tile_rank + size_t(j) * a.ep + r;
+        const int c = *q;
+        *q = run;
+        run += c;
+      }
+      if (p == P - 1) per_rank[r] = part[tid];
+    }
+    __syncthreads();
   }
-  for (int e = tid; e < a.E; e += 1024) {
-    int s = 0;
-    for (int j = 0; j < a.tiles; ++j) s += a.tile_expert[size_t(j) * a.E + e];
-    per_expert[e] = s;
+  {
+    const int P = pow2_floor(1024 / a.E);
+    const int e = tid / P, p = tid % P;
+    const int C = (a.tiles + P - 1) / P;
+    const int j0 = min(a.tiles, p * C), j1 = min(a.tiles, j0 + C);
+    int sum = 0;
+    if (e < a.E)
+      for (int j = j0; j < j1; ++j) sum += a.tile_expert[size_t(j) * a.E + e];
+    part[tid] = sum;
+    __syncthreads();
+    for (int off = P / 2; off >= 1; off >>= 1) {
+      if (p < off) part[tid] += part[tid + off];
+      __syncthreads();
+    }
+    if (e < a.E && p == 0) per_expert[e] = part[tid];
   }
 }
 

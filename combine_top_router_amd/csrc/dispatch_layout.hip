@@ -73,26 +73,32 @@ __global__ __launch_bounds__(kTile) void dl_count_kernel(DlArgs a) {
   for (int e = tid; e < a.E; e += kTile) a.tile_expert[size_t(tile) * a.E + e] = hist[e];
 }
 
-// Largest power of two <= n (n >= 1).
-__device__ __forceinline__ int pow2_floor(int n) { return 1 << (31 - __clz(n)); }
+// Threads per row when `rows` rows share 1024 threads over `n` tiles each: the
+// fewest (a power of two) that leave every thread at most one batch of 8.
+__device__ __forceinline__ int group_size(int rows, int n) {
+  int P = 1;
+  while (P * 2 * rows <= 1024 && P * 8 < n) P *= 2;
+  return P;
+}
 
 // One workgroup: rank r's tile counts become exclusive bases over the tiles in
 // order, and expert e's tile counts are summed. Each rank (then each expert)
-// gets a group of P threads (a power of two, P * rows <= 1024), each thread a
-// contiguous run of tiles whose loads are independent; the run sums are then
-// scanned (ranks) or reduced (experts) across the group in LDS.
+// gets a group of P threads (group_size), each thread a contiguous run of
+// tiles loaded in batches of independent loads; the run sums are then scanned
+// (ranks) or reduced (experts) across the group in LDS.
 __global__ __launch_bounds__(1024) void dl_scan_kernel(DlArgs a, int32_t* per_rank,
                                                       int32_t* per_expert) {
   __shared__ int32_t part[1024];
   const int tid = threadIdx.x;
   {
-    const int P = pow2_floor(1024 / a.ep);
+    const int P = group_size(a.ep, a.tiles);
     const int r = tid / P, p = tid % P;
     const int C = (a.tiles + P - 1) / P;
     const int j0 = min(a.tiles, p * C), j1 = min(a.tiles, j0 + C);
     int sum = 0;
     if (r < a.ep)
-      for (int j = j0; j < j1; ++j) sum += a.tile_rank[size_t(j) * a.ep + r];
+      batched_run(j0, j1, [&](int j) { return a.tile_rank[size_t(j) * a.ep + r]; },
+                  [&](int, int c) { sum += c; });
     part[tid] = sum;
     __syncthreads();
     // inclusive prefix of the run sums within each group (Hillis-Steele)
@@ -104,24 +110,24 @@ __global__ __launch_bounds__(1024) void dl_scan_kernel(DlArgs a, int32_t* per_ra
     }
     if (r < a.ep) {
       int run = part[tid] - sum;
-      for (int j = j0; j < j1; ++j) {
-        int32_t* q = a.tile_rank + size_t(j) * a.ep + r;
-        const int c = *q;
-        *q = run;
-        run += c;
-      }
+      batched_run(j0, j1, [&](int j) { return a.tile_rank[size_t(j) * a.ep + r]; },
+                  [&](int j, int c) {
+                    a.tile_rank[size_t(j) * a.ep + r] = run;
+                    run += c;
+                  });
       if (p == P - 1) per_rank[r] = part[tid];
     }
     __syncthreads();
   }
   {
-    const int P = pow2_floor(1024 / a.E);
+    const int P = group_size(a.E, a.tiles);
     const int e = tid / P, p = tid % P;
     const int C = (a.tiles + P - 1) / P;
     const int j0 = min(a.tiles, p * C), j1 = min(a.tiles, j0 + C);
     int sum = 0;
     if (e < a.E)
-      for (int j = j0; j < j1; ++j) sum += a.tile_expert[size_t(j) * a.E + e];
+      batched_run(j0, j1, [&](int j) { return a.tile_expert[size_t(j) * a.E + e]; },
+                  [&](int, int c) { sum += c; });
     part[tid] = sum;
     __syncthreads();
     for (int off = P / 2; off >= 1; off >>= 1) {

@@ -108,6 +108,21 @@ __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirs
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
+// Walks i = i0 .. i1-1 in batches of 8: load(i) for a whole batch is issued
+// before any value is used (the loads of a run are independent), then
+// use(i, value) in order. Returns nothing; use carries the state.
+template <class L, class U>
+__device__ __forceinline__ void batched_run(int i0, int i1, L&& load, U&& use) {
+  for (int i = i0; i < i1; i += 8) {
+    int v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = i + u < i1 ? load(i + u) : 0;
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (i + u < i1) use(i + u, v[u]);
+  }
+}
+
 // f(std::integral_constant<int, q>) for q = 0, 1, ..., in order: a fully
 // unrolled sequence whose steps can differ at compile time.
 template <class F, int... Q>

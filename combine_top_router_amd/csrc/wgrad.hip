@@ -23,9 +23,11 @@
 // Rows past the expert's count read as zeros through the buffer range of each
 // K slice (padding rows between experts hold stale data). An expert with no
 // rows gets a zero gradient. Workgroups are persistent; each XCD takes a
-// contiguous range of tile ids (expert-major), so the tiles of one expert,
-// which share both operands, sit behind the same L2. The next tile's first
-// slice is put in flight before a tile's epilogue.
+// contiguous range of tile ids (expert-major, then bands of 4 row tiles,
+// column tile major inside a band), so the tiles of one expert, which share
+// both operands, sit behind the same L2. A slice's loads go out one per
+// product of the step after the barrier, not back to back; the next tile's
+// first slice is put in flight before a tile's epilogue.
 #include "moe_internal.h"
 
 namespace moe {

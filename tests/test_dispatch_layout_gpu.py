@@ -19,6 +19,7 @@ moe = pytest.importorskip("combine_top_router_amd")
 CASES = [  # (workload, ep)
     ("tiny", 2), ("mixtral_8x7b", 8), ("qwen3_30b_a3b", 8), ("qwen3_30b_a3b", 64),
     ("deepseek_v3_ep8_share", 8), ("deepseek_v3_large", 8), ("deepseek_v3_large", 32),
+    ("deepseek_v3_large", 64),  # 256 tiles over 8-thread rank groups: several load batches
 ]
 
 

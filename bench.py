@@ -288,7 +288,7 @@ def main():
         calibrate_copy(args.calibrate_copy)
         return
     if args.gpus != 1:
-        print(f"bench.py runs one GPU only (got --gpus {args.gpus}): this build measures one "
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): it measures one "
               "GPU's share of the layer; sharding across GPUs is not implemented.",
               file=sys.stderr)
         sys.exit(2)

@@ -232,3 +232,15 @@ def test_grouped_data_gradient_leaves_padding_zero():
     dx = oexperts.grouped_swiglu_backward_data(xp, dy, offsets, counts, lambda e: ws[e])
     assert not dx[3].any() and not dx[6:].any()
     np.testing.assert_allclose(dx[4:6], oexperts.swiglu_backward(xp[4:6], *ws[1], dy[4:6])[0])
+
+
+def test_row_gradient_is_the_fp32_product_rounded_once_more():
+    # The row gradient is w * G as an fp32 product, then rounded to the bf16
+    # row dtype. Worked by hand: w = 11228502 * 2^-24 (an fp32 number) and
+    # G = 3 give the exact product 2 + 2^-7 + 2^-23, half an fp32 unit above
+    # the fp32 number 2 + 2^-7; that tie goes to 2 + 2^-7 (even significand),
+    # which is the midpoint between the bf16 numbers 2 and 2 + 2^-6 and ties
+    # to 2. Rounding the exact product to bf16 directly would give 2 + 2^-6.
+    w = np.array([[11228502 * 2.0 ** -24]], dtype=np.float32)
+    rows, written = ob.combine_backward_rows(np.array([[3.0]]), np.array([[0]]), w, 1)
+    assert written[0] and rows[0, 0] == 2.0

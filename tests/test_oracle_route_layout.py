@@ -182,6 +182,59 @@ def test_check_layout_catches_planted_mistakes():
         checks.check_layout(idx, bad2, 8, 2, 0, 4)
 
 
+
+def _consistent(L, src):
+    # a layout whose dst_row is the inverse of the given src_row, so that only
+    # the property a test breaks is wrong
+    dst = np.full(L["dst_row"].size, -1, dtype=np.int64)
+    rows = np.nonzero(src >= 0)[0]
+    dst[src[rows]] = rows
+    return dict(L, src_row=src.astype(np.int32),
+                dst_row=dst.reshape(L["dst_row"].shape).astype(np.int32))
+
+
+def test_check_layout_catches_each_planted_mistake_alone():
+    rng = np.random.default_rng(16)
+    idx = np.stack([rng.permutation(8)[:2] for _ in range(64)])
+    L = olayout.layout(idx, 8, 2, 0, 4)
+    checks.check_layout(idx, L, 8, 2, 0, 4)
+    o, c = L["offsets"].astype(np.int64), L["local_counts"].astype(np.int64)
+    e = int(np.nonzero((c >= 2) & (c % 4 != 0))[0][0])  # an expert with padding
+    a = o[e]
+    src = L["src_row"].astype(np.int64).copy()
+    src[[a, a + 1]] = src[[a + 1, a]]  # two rows of one expert swapped
+    with pytest.raises(AssertionError, match="unstable"):
+        checks.check_layout(idx, _consistent(L, src), 8, 2, 0, 4)
+    src = L["src_row"].astype(np.int64).copy()
+    src[a + c[e]], src[a + c[e] - 1] = src[a + c[e] - 1], -1  # last row moved into padding
+    with pytest.raises(AssertionError, match="padding misplaced"):
+        checks.check_layout(idx, _consistent(L, src), 8, 2, 0, 4)
+    src = L["src_row"].astype(np.int64).copy()
+    tail = int(o[-1])
+    if tail < src.size:
+        src[tail] = src[a]  # a tail row claims an assignment too
+        with pytest.raises(AssertionError):
+            checks.check_layout(idx, dict(L, src_row=src.astype(np.int32)), 8, 2, 0, 4)
+
+
+def test_check_route_catches_each_planted_mistake_alone():
+    rng = np.random.default_rng(17)
+    logits = rng.standard_normal((32, 16)).astype(np.float32)
+    idx, w = oroute.route(logits, 4)
+    checks.check_route(logits, idx, w)
+    swapped = idx.copy()
+    swapped[3, [0, 1]] = swapped[3, [1, 0]]
+    w_sw = w.copy()
+    w_sw[3, [0, 1]] = w_sw[3, [1, 0]]
+    with pytest.raises(AssertionError, match="descending logit order"):
+        checks.check_route(logits, swapped, w_sw)
+    fifth = np.argsort(-logits[5], kind="stable")[4]  # the best expert not selected
+    worse = idx.copy()
+    worse[5, 3] = fifth
+    with pytest.raises(AssertionError, match="unselected logit beats"):
+        checks.check_route(logits, worse, w)
+
+
 # ---------------------------------------------------------------- workloads
 
 @pytest.mark.parametrize("name", workloads.CONFIG_ORDER)

@@ -40,6 +40,29 @@ def test_bf16_matches_torch_on_fp32_values():
     assert (bf16.decode(want) == bf16.round_to_bf16(x.astype(np.float64))).all()
 
 
+
+def test_bf16_ends_of_the_range():
+    # Worked by hand from the bf16 format (8 significant bits, fp32's
+    # exponent range, round to nearest, ties to even):
+    #   the largest finite value (2 - 2^-7) * 2^127 stays finite;
+    #   the midpoint between it and 2^128 ties to the even neighbour, 2^128,
+    #   which overflows to infinity, and anything just below stays finite;
+    #   the smallest subnormal 2^-133 stays; 2^-134 is the midpoint between 0
+    #   and 2^-133 and goes to 0 (even); 3 * 2^-134 is the midpoint between
+    #   2^-133 and 2^-132 and goes to 2^-132 (even); zeros keep their sign.
+    mx = bf16.BF16_MAX
+    mid = 2.0 ** 128 - 2.0 ** 119
+    x = np.array([mx, -mx, mid, -mid, np.nextafter(np.float32(mid), np.float32(0)),
+                  np.finfo(np.float32).max, 2.0 ** -133, 2.0 ** -134, 3 * 2.0 ** -134,
+                  -0.0, 0.0], dtype=np.float32).astype(np.float64)
+    want = np.array([mx, -mx, np.inf, -np.inf, mx, np.inf, 2.0 ** -133, 0.0, 2.0 ** -132,
+                     -0.0, 0.0])
+    got = bf16.round_to_bf16(x)
+    assert (got == want).all() and (np.signbit(got) == np.signbit(want)).all()
+    tb = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).view(torch.int16)
+    assert (bf16.encode(x) == tb.numpy().view(np.uint16)).all()
+
+
 # ---------------------------------------------------------------- experts
 
 def test_swiglu_hand_example(swiglu_2x2):
@@ -170,6 +193,20 @@ def test_combine_error_matches_the_pages_benchmark(k, E, default_err):
     rel = lambda a: np.linalg.norm(a - exact) / np.linalg.norm(exact)  # noqa: E731
     assert abs(rel(fused) / 1.66e-3 - 1) < 0.05
     assert abs(rel(default) / default_err - 1) < 0.15
+
+
+
+def test_restore_default_rounds_the_weight_before_the_product():
+    # The default restore works in the activation dtype (DeepSpeed PR #8847,
+    # section "Problem"), so the routing weight is itself a bf16 number before
+    # it multiplies the row. Worked by hand: w = 1 + 2^-8 + 2^-10 lies above
+    # the midpoint 1 + 2^-8, so bf16(w) = 1 + 2^-7; times 3 that is
+    # 3.0234375, the midpoint between 3.015625 and 3.03125, which ties to
+    # the even 3.03125. Rounding only the product, 3w = 3.0146484375, would
+    # give 3.015625.
+    w = np.array([[1 + 2.0 ** -8 + 2.0 ** -10]], dtype=np.float32)
+    out = ocombine.restore_default(np.array([[3.0]]), np.array([[0]]), w)
+    assert out[0, 0] == 3.03125
 
 
 # ---------------------------------------------------------------- layer

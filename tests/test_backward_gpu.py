@@ -186,18 +186,32 @@ EXPERT_SHAPES = {
     # rows and must come back with zero weight gradients
     "empty_experts": (MoEConfig(name="empty_bwd", num_tokens=64, hidden=128, num_experts=32,
                                 top_k=1, inter=128, align=16), -1, None),
+    # row counts on the tile boundaries (given below, not routed): none, one,
+    # the 64-row small-tile limit, one 320-row tile and one row past it, a
+    # band of four row tiles plus one more; these counts are also the K
+    # extents of the weight gradients
+    "tile_edges": (MoEConfig(name="edges_bwd", num_tokens=3110, hidden=256, num_experts=11,
+                             top_k=1, inter=256, align=128), -1, None),
 }
+EXPERT_COUNTS = {"tile_edges": [0, 1, 33, 63, 64, 65, 319, 320, 321, 641, 1283]}
 EXPERT_DIST = {"empty_experts": "severe"}
 REL = 1e-2  # max|gpu - oracle| / max|oracle| per checked expert group
 
 
 def _expert_inputs(name):
     cfg, share, sample = EXPERT_SHAPES[name]
-    _, logits = workloads.gen.routing_inputs(cfg, EXPERT_DIST.get(name, "balanced"), 0,
-                                             device="cpu")
-    idx = oroute.select(logits.numpy(), cfg.top_k)
-    L = olayout.layout(idx, cfg.num_experts, cfg.ep_size, share, cfg.align)
-    m_cap = cfg.m_cap(share)
+    if name in EXPERT_COUNTS:
+        counts = np.array(EXPERT_COUNTS[name])
+        assert counts.size == cfg.num_experts and counts.sum() == cfg.num_tokens
+        padded = (counts + cfg.align - 1) // cfg.align * cfg.align
+        L = {"local_counts": counts, "offsets": np.concatenate([[0], np.cumsum(padded)])}
+        m_cap = int(L["offsets"][-1]) + cfg.align  # a tail past the last group
+    else:
+        _, logits = workloads.gen.routing_inputs(cfg, EXPERT_DIST.get(name, "balanced"), 0,
+                                                 device="cpu")
+        idx = oroute.select(logits.numpy(), cfg.top_k)
+        L = olayout.layout(idx, cfg.num_experts, cfg.ep_size, share, cfg.align)
+        m_cap = cfg.m_cap(share)
     x_perm = workloads.gen.expert_outputs(cfg, m_cap, 1, device="cpu")  # stand-in rows
     dy = workloads.gen.expert_outputs(cfg, m_cap, 2, device="cpu")
     experts = list(cfg.local_experts(share))

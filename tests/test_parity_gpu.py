@@ -326,6 +326,51 @@ def test_swiglu_orientation_closed_form():
     assert rel_max(f64(y[:rows]), want) <= 1e-2
 
 
+# Row counts on every tile boundary of the grouped GEMMs: none, one, the
+# 32-row block edges, the 64-row small-tile limit, one 320-row tile and one
+# row past it, two and four tiles and one row past them (a band of four row
+# tiles plus a tail band). H = 512 takes the 320 x 256 tiles for both
+# products; H = 384 gives down an output width that is not a multiple of 256,
+# which takes the 256 x 128 tiles.
+EDGE_COUNTS = [0, 1, 31, 32, 33, 63, 64, 65, 96, 255, 256, 257, 319, 320, 321, 640, 641,
+               1280, 1283, 0]
+
+
+@pytest.mark.parametrize("H,I", [(512, 256), (384, 128)])
+def test_grouped_swiglu_tile_edges(H, I):
+    announce(f"grouped_swiglu tile edges H={H} I={I}")
+    rng = np.random.default_rng(H + I)
+    counts = np.array(EDGE_COUNTS)
+    E = counts.size
+    padded = (counts + 127) // 128 * 128
+    offsets = np.concatenate([[0], np.cumsum(padded)])
+    m_cap = int(offsets[-1]) + 128  # a tail past the last group
+    w1 = obf16.round_to_bf16(rng.standard_normal((E, H, I)) / np.sqrt(H))
+    w3 = obf16.round_to_bf16(rng.standard_normal((E, H, I)) / np.sqrt(H))
+    w2 = obf16.round_to_bf16(rng.standard_normal((E, I, H)) / np.sqrt(I))
+    x = np.full((m_cap, H), np.nan)
+    for e in range(E):
+        a = offsets[e]
+        x[a:a + counts[e]] = obf16.round_to_bf16(rng.standard_normal((counts[e], H)))
+    dev = lambda a: from_bits(obf16.encode(a))  # noqa: E731
+    h = torch.zeros((m_cap, I), dtype=torch.int16, device="cuda").fill_(0x7FC1)
+    y = torch.zeros((m_cap, H), dtype=torch.int16, device="cuda").fill_(0x7FC1)
+    h, y = h.view(torch.bfloat16), y.view(torch.bfloat16)
+    moe.grouped_swiglu(dev(x), i32(offsets), i32(counts), moe.pack_weights(dev(w1)),
+                       moe.pack_weights(dev(w3)), moe.pack_weights(dev(w2)), h=h, out=y)
+    got = f64(y)
+    for e in range(E):
+        a, c = int(offsets[e]), int(counts[e])
+        if c:
+            want = oexperts.swiglu(x[a:a + c], w1[e], w3[e], w2[e])
+            assert np.isfinite(got[a:a + c]).all(), (e, c)
+            assert rel_max(got[a:a + c], want) <= 1e-2, (e, c, rel_max(got[a:a + c], want))
+        # rows past the group (padding, and the tail after the last group) are never written
+        end = int(offsets[e + 1]) if e + 1 < E else m_cap
+        assert (bits(y[a + c:end]) == 0x7FC1).all(), (e, c)
+        assert (bits(h[a + c:end]) == 0x7FC1).all(), (e, c)
+
+
 # ---------------------------------------------------------------- combine
 
 def _combine_tokens(cfg, rng, full):

@@ -178,7 +178,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const u32x4* __restrict__ 
   }
 
   // kU vectors per lane per round, all of a slot's loads issued before its
-  // products, so a wavefront keeps kU KiB per slot in flight
+  // products, so a wavefront keeps kU KiB per slot in flight. With at most two
+  // slots (known at compile time) every slot's loads go out before the first
+  // product, so the token's whole round of reads is in flight at once.
+  constexpr bool ALL = K > 0 && K <= 2;
   constexpr int kU = 4;
   u32x4* dst = out + t * hv;
   for (int v0 = lane; v0 < hv; v0 += kU * kWave) {
@@ -187,7 +190,33 @@ __global__ __launch_bounds__(256) void combine_kernel(const u32x4* __restrict__ 
     for (int u = 0; u < kU; ++u)
 #pragma unroll
       for (int q = 0; q < NV; ++q) acc[u][q] = 0.f;
-    for (int j = 0; j < nv; ++j) {
+    if constexpr (ALL) {
+      u32x4 in[KM][kU];
+#pragma unroll
+      for (int j = 0; j < KM; ++j) {
+        if (j < nv) {
+          const u32x4* src = y + rows[j] * hv;
+#pragma unroll
+          for (int u = 0; u < kU; ++u)
+            if (v0 + u * kWave < hv) in[j][u] = __builtin_nontemporal_load(src + v0 + u * kWave);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < KM; ++j) {
+        if (j < nv) {
+#pragma unroll
+          for (int u = 0; u < kU; ++u) {
+            if (v0 + u * kWave < hv) {
+              float f[NV];
+              R::load(in[j][u], f);
+#pragma unroll
+              for (int q = 0; q < NV; ++q) acc[u][q] = acc[u][q] + w[j] * f[q];
+            }
+          }
+        }
+      }
+    }
+    for (int j = 0; !ALL && j < nv; ++j) {
       u32x4 in[kU];
       const u32x4* src = y + rows[j] * hv;
 #pragma unroll

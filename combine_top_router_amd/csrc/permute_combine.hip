@@ -177,12 +177,12 @@ __global__ __launch_bounds__(256) void combine_kernel(const u32x4* __restrict__ 
     }
   }
 
-  // kU vectors per lane per round, all of a slot's loads issued before its
-  // products, so a wavefront keeps kU KiB per slot in flight. With at most two
-  // slots (known at compile time) every slot's loads go out before the first
-  // product, so the token's whole round of reads is in flight at once.
-  constexpr bool ALL = K > 0 && K <= 2;
+  // kU vectors per lane per round. The local slots go in groups of GS (the
+  // whole token at top-k <= 2, pairs above): a group's loads are all issued
+  // before its first product, so a wavefront keeps GS * kU KiB in flight, and
+  // the products still run in slot order.
   constexpr int kU = 4;
+  constexpr int GS = (K > 0 && K <= 2) ? K : 2;
   u32x4* dst = out + t * hv;
   for (int v0 = lane; v0 < hv; v0 += kU * kWave) {
     float acc[kU][NV];
@@ -190,45 +190,30 @@ __global__ __launch_bounds__(256) void combine_kernel(const u32x4* __restrict__ 
     for (int u = 0; u < kU; ++u)
 #pragma unroll
       for (int q = 0; q < NV; ++q) acc[u][q] = 0.f;
-    if constexpr (ALL) {
-      u32x4 in[KM][kU];
+    // at top-k <= 2 one group (a compile-time trip count, so constant indices)
+    for (int j0 = 0; (K > 0 && K <= 2) ? j0 < GS : j0 < nv; j0 += GS) {
+      u32x4 in[GS][kU];
 #pragma unroll
-      for (int j = 0; j < KM; ++j) {
-        if (j < nv) {
-          const u32x4* src = y + rows[j] * hv;
+      for (int g = 0; g < GS; ++g) {
+        if (j0 + g < nv) {
+          const u32x4* src = y + rows[j0 + g] * hv;
 #pragma unroll
           for (int u = 0; u < kU; ++u)
-            if (v0 + u * kWave < hv) in[j][u] = __builtin_nontemporal_load(src + v0 + u * kWave);
+            if (v0 + u * kWave < hv) in[g][u] = __builtin_nontemporal_load(src + v0 + u * kWave);
         }
       }
 #pragma unroll
-      for (int j = 0; j < KM; ++j) {
-        if (j < nv) {
+      for (int g = 0; g < GS; ++g) {
+        if (j0 + g < nv) {
 #pragma unroll
           for (int u = 0; u < kU; ++u) {
             if (v0 + u * kWave < hv) {
               float f[NV];
-              R::load(in[j][u], f);
+              R::load(in[g][u], f);
 #pragma unroll
-              for (int q = 0; q < NV; ++q) acc[u][q] = acc[u][q] + w[j] * f[q];
+              for (int q = 0; q < NV; ++q) acc[u][q] = acc[u][q] + w[j0 + g] * f[q];
             }
           }
-        }
-      }
-    }
-    for (int j = 0; !ALL && j < nv; ++j) {
-      u32x4 in[kU];
-      const u32x4* src = y + rows[j] * hv;
-#pragma unroll
-      for (int u = 0; u < kU; ++u)
-        if (v0 + u * kWave < hv) in[u] = __builtin_nontemporal_load(src + v0 + u * kWave);
-#pragma unroll
-      for (int u = 0; u < kU; ++u) {
-        if (v0 + u * kWave < hv) {
-          float f[NV];
-          R::load(in[u], f);
-#pragma unroll
-          for (int q = 0; q < NV; ++q) acc[u][q] = acc[u][q] + w[j] * f[q];
         }
       }
     }

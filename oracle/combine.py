@@ -21,7 +21,8 @@ rounded once to bf16 (reading: "accumulates in FP32" taken literally, IEEE
 fp32 operations, no fused multiply-add). A slot whose row lives on another
 GPU share has ``dst_row = -1`` and contributes nothing; a token with no local
 slot gives a zero row. ``combine_exact`` is the same sum in fp64, the
-reference the pages measure the error against; ``restore_default`` is the
+reference the pages measure the error against, and ``combine_error_bound``
+bounds the FP32 restore's distance from it a priori; ``restore_default`` is the
 activation-dtype restore of section "Problem", kept for the error contrast
 of section "Benchmark".
 """
@@ -76,6 +77,44 @@ def combine_exact(y, dst_row, topk_w, validate_coverage: bool = False) -> np.nda
         m = r >= 0
         out[m] += w[m, s][:, None] * y[r[m]]
     return out
+
+
+def combine_error_bound(y, dst_row, topk_w) -> np.ndarray:
+    """A-priori bound [T, H] on |fused restore - exact sum|, fp64.
+
+    The fused restore (section "Problem": FP32 accumulation; section
+    "Benchmark": the error left against FP64 is the bf16 output rounding)
+    forms n fp32 products and adds them in fp32, n being the token's local
+    slots, then rounds once to bf16. Each product and each addition is one
+    correctly rounded fp32 operation (unit roundoff u = 2^-24), so by the
+    standard error analysis of a recursively summed dot product
+    |fp32 sum - exact| <= gamma_n * sum_s |w_s y_s|, gamma_n = n u / (1 - n u),
+    plus at most one fp32 subnormal spacing (2^-149) per product for
+    underflow. The bf16 rounding adds at most half a bf16 unit of the fp32
+    value, which lies within |exact| + that bound; half a unit at a value in
+    [2^e, 2^(e+1)) is 2^(e-8), never below the subnormal half-spacing 2^-134.
+    """
+    y = np.asarray(y, dtype=np.float64)
+    dst = np.asarray(dst_row, dtype=np.int64)
+    w = np.asarray(topk_w).astype(np.float32).astype(np.float64)
+    T, k = dst.shape
+    mag = np.zeros((T, y.shape[1]), dtype=np.float64)
+    exact = np.zeros_like(mag)
+    n = np.zeros(T, dtype=np.int64)
+    for s in range(k):
+        r = dst[:, s]
+        m = r >= 0
+        p = w[m, s][:, None] * y[r[m]]
+        exact[m] += p
+        mag[m] += np.abs(p)
+        n += m
+    u = 2.0 ** -24
+    gamma = (n * u / (1.0 - n * u))[:, None]
+    fp32_err = gamma * mag + n[:, None] * 2.0 ** -149
+    top = np.abs(exact) + fp32_err
+    _, e = np.frexp(top)  # top = f * 2^e, 0.5 <= f < 1: top in [2^(e-1), 2^e)
+    half_unit = np.ldexp(1.0, np.maximum(e.astype(np.int64) - 9, -134))
+    return fp32_err + np.where(top > 0, half_unit, 0.0)
 
 
 def restore_default(y, dst_row, topk_w) -> np.ndarray:

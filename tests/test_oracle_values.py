@@ -282,3 +282,97 @@ def test_score_before_and_after_the_experts_agree_for_identity_experts():
     exact = ocombine.combine_exact(opermute.permute(x, L["src_row"], k), L["dst_row"], w)
     assert np.abs(pre - exact).max() <= 2.0 ** -6 * np.abs(exact).max()
     assert np.abs(post - exact).max() <= 2.0 ** -7 * np.abs(exact).max()
+
+
+def test_permute_weighted_rounds_the_fp32_product_once():
+    # Score applied before the experts (DeepSpeed PR #8847, section "Change",
+    # score_apply="pre"): the row is the fp32 product w * x rounded once to
+    # bf16. Worked by hand, w = 1 + 2^-9 + 2^-17 (an fp32 number) and
+    # x = 2 - 2^-7 (a bf16 number): the exact product is
+    # 2 - 2^-7 + 2^-8 - 2^-16 + 2^-16 - 2^-24 = 2 - 2^-8 - 2^-24. It sits half
+    # way between the fp32 neighbours 2 - 2^-8 - 2^-23 (odd significand) and
+    # 2 - 2^-8 (even), so the fp32 product is 2 - 2^-8: the midpoint of the
+    # bf16 neighbours 2 - 2^-7 (odd) and 2, which ties to the even 2.0.
+    # The two other readings give 2 - 2^-7 = 1.9921875 here:
+    #  * rounding the weight to bf16 first: w is below the midpoint 1 + 2^-8,
+    #    so bf16(w) = 1 and bf16(1 * x) = x;
+    #  * rounding the exact product straight to bf16: it lies below the
+    #    midpoint 2 - 2^-8.
+    # (No single input can make all three readings differ: rounding w to bf16
+    # moves the product by at most one bf16 unit of it, so the weight-first
+    # value always equals one of the other two. The second case below covers
+    # the weight-first reading where the other two agree.)
+    w = np.array([[1 + 2.0 ** -9 + 2.0 ** -17]], dtype=np.float32)
+    assert float(w[0, 0]) == 1 + 2.0 ** -9 + 2.0 ** -17
+    x = np.array([[2 - 2.0 ** -7]])
+    rows, written = opermute.permute_weighted(x, np.array([[0]]), w, 1)
+    assert written.tolist() == [True]
+    assert rows[0, 0] == 2.0
+    # Second case: w = 1 + 2^-8 + 2^-10, x = 1.5. The product 1.50732421875 is
+    # exact in fp32 and above the bf16 midpoint 1.50390625, so the row is
+    # 1.5078125. Rounding the weight first gives bf16(w) = 1 + 2^-7 (w lies
+    # above the midpoint 1 + 2^-8), and 1.5 * (1 + 2^-7) = 1.51171875 is the
+    # midpoint of 1.5078125 (odd) and 1.515625 (even): 1.515625.
+    w2 = np.array([[1 + 2.0 ** -8 + 2.0 ** -10]], dtype=np.float32)
+    rows2, _ = opermute.permute_weighted(np.array([[1.5]]), np.array([[0]]), w2, 1)
+    assert rows2[0, 0] == 1.5078125
+    # rows no slot points at stay unwritten
+    rows3, written3 = opermute.permute_weighted(np.array([[1.0], [2.0]]), np.array([[1], [-1]]),
+                                                np.ones((2, 1), np.float32), 3)
+    assert written3.tolist() == [False, True, False] and rows3[1, 0] == 1.0
+
+
+# ---------------------------------------------------------------- combine error bound
+
+def test_combine_bound_holds_for_the_fp32_sum():
+    # a-priori bound of the fused restore against the exact sum: gamma_n
+    # (n = local slots) times sum |w y|, plus half a bf16 unit of the result
+    rng = np.random.default_rng(21)
+    T, k, H, R = 512, 8, 64, 4096
+    dst = np.stack([rng.permutation(R)[:k] for _ in range(T)])
+    dst[::7, 3] = -1  # some slots of other shares
+    w = rng.random((T, k)).astype(np.float32)
+    y = bf16.round_to_bf16(rng.standard_normal((R, H)))
+    exact = ocombine.combine_exact(y, dst, w)
+    bound = ocombine.combine_error_bound(y, dst, w)
+    fused = ocombine.combine_bf16(y, dst, w)
+    assert (np.abs(fused - exact) <= bound).all()
+    # a sum on a bf16 midpoint: 1 + 2^-8 ties to 1.0, an error of exactly
+    # half a bf16 unit, which is all but the whole bound
+    y1, w1, d1 = np.array([[1.0], [2.0 ** -8]]), np.ones((1, 2), np.float32), np.array([[0, 1]])
+    err1 = abs(ocombine.combine_bf16(y1, d1, w1)[0, 0] - (1 + 2.0 ** -8))
+    b1 = ocombine.combine_error_bound(y1, d1, w1)[0, 0]
+    assert err1 == 2.0 ** -8 and 0.99 * b1 < err1 <= b1
+    # rows that cancel: the fp32 product (1 + 2^-23)(1 + 2^-7) loses its 2^-30
+    # term, the sum with -(1 + 2^-7) is 2^-23 where the exact value is
+    # 2^-23 + 2^-30. That error is twice half a bf16 unit of the result
+    # (2^-31): a bound of half a unit alone would reject the FP32 restore,
+    # the gamma_n term admits it
+    y2 = np.array([[1.0 + 2.0 ** -7], [-(1.0 + 2.0 ** -7)]])
+    w2 = np.array([[1.0 + 2.0 ** -23, 1.0]], dtype=np.float32)
+    d2 = np.array([[0, 1]])
+    err2 = abs(ocombine.combine_bf16(y2, d2, w2)[0, 0] - ocombine.combine_exact(y2, d2, w2)[0, 0])
+    assert err2 == 2.0 ** -30
+    assert err2 <= ocombine.combine_error_bound(y2, d2, w2)[0, 0]
+
+
+def test_combine_bound_rejects_plausible_mistakes():
+    # the bound is tight enough that a dropped slot, a bf16 running sum (the
+    # default restore) or bf16-rounded weights break it on Gaussian rows
+    rng = np.random.default_rng(22)
+    T, E, k, H = 2048, 64, 8, 128
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    idx, w = oroute.route(logits, k)
+    L = olayout.layout(idx, E, 1, -1, 1)
+    y = bf16.round_to_bf16(rng.standard_normal((L["m_cap"], H)))
+    dst = L["dst_row"]
+    exact = ocombine.combine_exact(y, dst, w)
+    bound = ocombine.combine_error_bound(y, dst, w)
+    assert not (np.abs(ocombine.restore_default(y, dst, w) - exact) <= bound).all()
+    dropped = dst.copy()
+    dropped[:, -1] = -1
+    assert not (np.abs(ocombine.combine_bf16(y, dropped, w) - exact) <= bound).all()
+    wb = bf16.round_to_bf16(w.astype(np.float64))
+    assert not (np.abs(ocombine.combine_bf16(y, dst, wb) - exact) <= bound).all()
+    # the exact sum rounded once obeys it (half a unit is inside the bound)
+    assert (np.abs(bf16.round_to_bf16(exact) - exact) <= bound).all()

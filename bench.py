@@ -1,19 +1,29 @@
 """MoE-layer throughput on one MI355X.
 
-    python bench.py [--gpus 1] [--steps 30] [--warmup 30] [--workload mixtral_8x7b] [--dist ...]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 10] [--workload deepseek_v3_large]
+                    [--dist ...] [--no-backward] [--no-extra] [--no-flush] [--no-cpu-baseline]
 
 One step = one pass of the whole single-GPU layer over one batch of seeded
 synthetic input already resident in HBM:
 
     moe_route -> moe_layout -> moe_permute -> moe_grouped_gate_up -> moe_grouped_down -> moe_combine
 
-Prints ONE JSON line (everything else goes to stderr):
-  value       tokens/s of the layer (for an EP share: the share's own tokens per
-              rank, T/ep, per step)
-  roofline    the dominant kernel's algorithmic FLOP/s (or bytes/s) per launch over
-              its average launch time, measured with HIP events on the stream the
-              library launches on, against the MI355X datasheet peak
-  stages      the same per stage
+The default workload is the large DeepSeek-V3-shaped layer (65536 tokens,
+hidden 7168, 256 experts all local, top-8, intermediate 2048, bf16, severe
+skew), the largest that fits one GPU. Prints ONE JSON line (everything else
+goes to stderr):
+  value        tokens/s of the layer, steps run back to back (for an EP share:
+               the share's own tokens per rank, T/ep, per step)
+  roofline     the dominant kernel's algorithmic FLOP/s (or bytes/s) per launch over
+               its average launch time, measured with HIP events on the stream the
+               library launches on, against the MI355X datasheet peak
+  stages       the same per stage (back to back, as inside a model)
+  stages_cold  the same per stage from a cold cache: a 512 MB buffer is read and
+               written before every stage, outside its events
+  backward     the training and variant calls, each timed on its own
+  extra        the one-GPU share of the DeepSeek-V3 EP=8 layer (balanced
+               routing) as its own step, and the combine alone at the large
+               DeepSeek-V3 shape ([T*8, H] expert rows, no padding), warm and cold
   cpu_baseline the CPU oracle timed on a bounded sample of the same workload
 """
 from __future__ import annotations
@@ -38,14 +48,20 @@ def log(*a):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
-    ap.add_argument("--warmup", type=int, default=30)
-    ap.add_argument("--workload", default="mixtral_8x7b")
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="deepseek_v3_large")
     ap.add_argument("--dist", default=None)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip timing the backward calls")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the extra workloads (the DeepSeek-V3 EP=8 share and the "
+                         "combine-only case)")
+    ap.add_argument("--no-flush", action="store_true",
+                    help="skip the per-stage timing from a cold cache (a 512 MB buffer "
+                         "read and written before every stage, outside its events)")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for the CPU baseline sample")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -282,28 +298,75 @@ def time_backward(args, cfg, layer, moe, stream, t_loc, n_loc, weights, x):
     return out
 
 
-def main():
-    args = parse()
-    if args.calibrate_copy:
-        calibrate_copy(args.calibrate_copy)
-        return
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): it measures one "
-              "GPU's share of the layer; sharding across GPUs is not implemented.",
-              file=sys.stderr)
-        sys.exit(2)
+FLUSH_BYTES = 512 << 20  # twice the 256 MB last-level cache
 
+
+class Flusher:
+    """Reads and writes a 512 MB buffer: after it, nothing a stage touched
+    before is left in the L2s or the last-level cache."""
+
+    def __init__(self, dev):
+        import torch
+        self.buf = torch.zeros(FLUSH_BYTES // 4, dtype=torch.int32, device=dev)
+
+    def __call__(self):
+        self.buf.add_(1)
+
+
+def layer_work(cfg, layer):
+    """Algorithmic bytes (HBM stages) and (flops, bytes) (GEMM stages) of one
+    step on this batch's routing, read once outside any timed region."""
+    import numpy as np
+    counts = layer.L.local_counts.cpu().numpy().astype(np.int64)
+    dst = layer.L.dst_row.cpu().numpy()
+    n_loc = int(counts.sum())
+    t_loc = int((dst >= 0).any(axis=1).sum())
+    e_act = int((counts > 0).sum())
+    T, H, I, E, k = cfg.num_tokens, cfg.hidden, cfg.inter, cfg.num_experts, cfg.top_k
+    N = T * k
+    wbytes = float(e_act) * H * I * 2  # one expert matrix of each active expert
+    work = {
+        "route": ("hbm", T * E * 4 + N * 8),
+        "layout": ("hbm", N * 4 * 2 + n_loc * 4),
+        "permute": ("hbm", (t_loc + n_loc) * H * 2),
+        "gate_up": ("gemm", (4.0 * n_loc * H * I, 2 * wbytes + n_loc * (H + I) * 2)),
+        "down": ("gemm", (2.0 * n_loc * H * I, wbytes + n_loc * (I + H) * 2)),
+        "combine": ("hbm", n_loc * H * 2 + N * 8 + T * H * 2),
+    }
+    return work, n_loc, t_loc
+
+
+def stage_times(stages, stream, n, flush=None):
+    """Mean time of each stage over n steps, an event between every two
+    stages. With ``flush``, the caches are flushed before every stage, outside
+    its events: the stage then starts from a cold cache."""
+    import numpy as np
+    import torch
+    n_st = len(stages)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * n_st)] for _ in range(n)]
+    for s in range(n):
+        for i, (_, run) in enumerate(stages):
+            if flush is not None:
+                flush()
+            evs[s][2 * i].record(stream)
+            run()
+            evs[s][2 * i + 1].record(stream)
+    torch.cuda.synchronize()
+    return {name: float(np.mean([evs[s][2 * i].elapsed_time(evs[s][2 * i + 1])
+                                 for s in range(n)]))
+            for i, (name, _) in enumerate(stages)}
+
+
+def run_layer(cfg, dist, args, dev, flush):
+    """Builds the layer on seeded inputs and times it. Returns the record
+    parts and what the CPU baseline and the backward timing need."""
     import numpy as np
     import torch
 
     import combine_top_router_amd as moe
     import workloads
 
-    cfg = workloads.get(args.workload)
-    dist = args.dist or cfg.dists[0]
     share = cfg.local_rank
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
     log(f"workload {cfg.name} dist {dist} share {share}: generating inputs")
     x, logits = workloads.gen.routing_inputs(cfg, dist, args.seed, device=dev)
     w1, w3, w2 = workloads.gen.expert_weights(cfg, cfg.local_experts(share), args.seed, device=dev)
@@ -323,41 +386,12 @@ def main():
         ws = [wev[i].elapsed_time(wev[i + 1]) for i in range(args.warmup)]
         log("warmup step ms: first %.3f, last %.3f, min %.3f" % (ws[0], ws[-1], min(ws)))
 
-    # algorithmic work of this batch (read once, outside the timed region)
-    counts = layer.L.local_counts.cpu().numpy().astype(np.int64)
-    dst = layer.L.dst_row.cpu().numpy()
-    n_loc = int(counts.sum())
-    t_loc = int((dst >= 0).any(axis=1).sum())
-    e_act = int((counts > 0).sum())
-    T, H, I, E, k = cfg.num_tokens, cfg.hidden, cfg.inter, cfg.num_experts, cfg.top_k
-    N = T * k
-    wbytes = float(e_act) * H * I * 2  # one expert matrix of each active expert
-    work = {
-        "route": ("hbm", T * E * 4 + N * 8),
-        "layout": ("hbm", N * 4 * 2 + n_loc * 4),
-        "permute": ("hbm", (t_loc + n_loc) * H * 2),
-        "gate_up": ("gemm", (4.0 * n_loc * H * I, 2 * wbytes + n_loc * (H + I) * 2)),
-        "down": ("gemm", (2.0 * n_loc * H * I, wbytes + n_loc * (I + H) * 2)),
-        "combine": ("hbm", n_loc * H * 2 + N * 8 + T * H * 2),
-    }
-
+    work, n_loc, t_loc = layer_work(cfg, layer)
     n_st = len(stages)
-
-    def per_stage_events(n):
-        # n steps with an event between every two stages: the stage breakdown
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_st + 1)] for _ in range(n)]
-        for s in range(n):
-            evs[s][0].record(stream)
-            for i, (_, run) in enumerate(stages):
-                run()
-                evs[s][i + 1].record(stream)
-        torch.cuda.synchronize()
-        return {name: float(np.mean([evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(n)]))
-                for i, (name, _) in enumerate(stages)}
 
     # the dominant stage, from untimed steps; the timed steps record events only
     # around it (an event between every two stages adds GPU time to each step)
-    probe = per_stage_events(3)
+    probe = stage_times(stages, stream, 3)
     dom_i = max(range(n_st), key=lambda i: probe[stages[i][0]])
     dom = stages[dom_i][0]
     dev_ = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
@@ -376,41 +410,131 @@ def main():
     dom_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in dev_]))
 
     # the other stages' times from as many steps again, after the timed region
-    stage_ms = per_stage_events(args.steps)
+    stage_ms = stage_times(stages, stream, args.steps)
     stage_ms[dom] = dom_ms
-    step_ms = elapsed / args.steps * 1e3
-    tokens_per_step = T // cfg.ep_size
-    value = tokens_per_step * args.steps / elapsed
+    out = {
+        "value": cfg.num_tokens // cfg.ep_size * args.steps / elapsed,
+        "ms_per_step": elapsed / args.steps * 1e3,
+        "dom": dom,
+        "local_rows": n_loc,
+        "stages": {name: roof_entry(ms, *work[name]) for name, ms in stage_ms.items()},
+    }
+    if flush is not None:
+        cold = stage_times(stages, stream, args.steps, flush)
+        out["stages_cold"] = {name: roof_entry(ms, *work[name]) for name, ms in cold.items()}
+    return out, (layer, x, logits, (w1, w3, w2), stream, t_loc, n_loc)
 
-    stage_out = {name: roof_entry(ms, *work[name]) for name, ms in stage_ms.items()}
+
+def roofline_of(cfg, stage_out, dom):
     d = stage_out[dom]
     traffic = traffic_record(dom, cfg.name) if dom in ("gate_up", "down") else None
     if d["bound"] == "mfma":
-        roof = {"bound": "mfma", "kernel": dom, "achieved": d["TFLOP/s"],
+        return {"bound": "mfma", "kernel": dom, "achieved": d["TFLOP/s"],
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": d["frac"],
                 "traffic": traffic}
-    else:
-        roof = {"bound": "hbm", "kernel": dom, "achieved": d["GB/s"], "peak": PEAK_HBM_GBS,
-                "unit": "GB/s", "frac": d["frac"], "traffic": traffic}
+    return {"bound": "hbm", "kernel": dom, "achieved": d["GB/s"], "peak": PEAK_HBM_GBS,
+            "unit": "GB/s", "frac": d["frac"], "traffic": traffic}
 
+
+def combine_only(cfg, args, dev, flush):
+    """The fused restore on its own at this workload's routing: expert outputs
+    [T*k, H] bf16 in expert order with no padding (alignment 1), N(0, 1), into
+    [T, H]; timed back to back and from a cold cache."""
+    import numpy as np
+    import torch
+
+    import combine_top_router_amd as moe
+    import workloads
+
+    T, H, k = cfg.num_tokens, cfg.hidden, cfg.top_k
+    _, logits = workloads.gen.routing_inputs(cfg, cfg.dists[0], args.seed, device=dev)
+    idx, w = moe.route(logits, k)
+    L = moe.layout(idx, cfg.num_experts, 1, -1, 1)
+    del logits
+    y = workloads.gen.expert_outputs(cfg, T * k, seed=7, device=dev)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    run = lambda: moe.ops.combine(y, L.dst_row, w, out=out)  # noqa: E731
+    for _ in range(3):
+        run()
+    nbytes = T * k * H * 2 + T * k * 8 + T * H * 2
+    rec = {"shape": f"y [{T * k}, {H}] bf16, alignment 1 -> out [{T}, {H}]",
+           "bytes": nbytes}
+    for name, fl in (("warm", None), ("cold", flush)):
+        if name == "cold" and fl is None:
+            continue
+        ms = stage_times([("combine", run)], stream, max(args.steps, 5), fl)["combine"]
+        rec[name] = roof_entry(ms, "hbm", nbytes)
+    del y, out, L
+    return rec
+
+
+def main():
+    args = parse()
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): it measures one "
+              "GPU's share of the layer; sharding across GPUs is not implemented.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import combine_top_router_amd as moe
+    import workloads
+
+    cfg = workloads.get(args.workload)
+    dist = args.dist or cfg.dists[0]
+    share = cfg.local_rank
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    flush = None if args.no_flush else Flusher(dev)
+
+    head, (layer, x, logits, weights, stream, t_loc, n_loc) = run_layer(cfg, dist, args, dev,
+                                                                        flush)
+    roof = roofline_of(cfg, head["stages"], head["dom"])
     backward = None if args.no_backward else time_backward(args, cfg, layer, moe, stream,
-                                                            t_loc, n_loc, (w1, w3, w2), x)
-
+                                                            t_loc, n_loc, weights, x)
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
-        cpu = cpu_baseline(cfg, dist, (x, logits, w1, w3, w2, share), args.cpu_budget)
+        cpu = cpu_baseline(cfg, dist, (x, logits) + tuple(weights) + (share,), args.cpu_budget)
+    del layer, x, logits, weights
+    torch.cuda.empty_cache()
+
+    extra = {}
+    if not args.no_extra:
+        # the one-GPU share of the DeepSeek-V3 EP=8 layer, balanced routing
+        if cfg.name != "deepseek_v3_ep8_share":
+            c4 = workloads.get("deepseek_v3_ep8_share")
+            rec, parts = run_layer(c4, "balanced", args, dev, flush)
+            del parts
+            torch.cuda.empty_cache()
+            extra["deepseek_v3_ep8_share"] = {
+                "value": round(rec["value"], 1), "unit": "tokens/s per GPU (1024 tokens per rank)",
+                "ms_per_step": round(rec["ms_per_step"], 4), "routing": "balanced",
+                "local_rows": rec["local_rows"], "roofline": roofline_of(c4, rec["stages"], rec["dom"]),
+                "stages": rec["stages"], "stages_cold": rec.get("stages_cold")}
+        # the restore alone at the large DeepSeek-V3 shape
+        big = workloads.get("deepseek_v3_large")
+        extra["combine_only_deepseek_v3_large"] = combine_only(big, args, dev, flush)
+        torch.cuda.empty_cache()
 
     rec = {
         "metric": "MoE layer tokens/s on 1 MI355X; % HBM roofline (perm/combine), % MFMA (GEMM)",
-        "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(step_ms, 4), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": cfg.name, "tokens": T, "hidden": H, "experts": E,
-                   "local_experts": len(cfg.local_experts(share)), "top_k": k, "inter": I,
-                   "ep_size": cfg.ep_size, "local_rank": share, "align": cfg.align,
-                   "routing": dist, "local_rows": n_loc, "seed": args.seed},
-        "roofline": roof, "stages": stage_out, "backward": backward, "cpu_baseline": cpu,
+        "value": round(head["value"], 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(head["ms_per_step"], 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "tokens": cfg.num_tokens, "hidden": cfg.hidden,
+                   "experts": cfg.num_experts, "local_experts": len(cfg.local_experts(share)),
+                   "top_k": cfg.top_k, "inter": cfg.inter, "ep_size": cfg.ep_size,
+                   "local_rank": share, "align": cfg.align, "routing": dist,
+                   "local_rows": head["local_rows"], "seed": args.seed},
+        "roofline": roof, "stages": head["stages"], "stages_cold": head.get("stages_cold"),
+        "backward": backward, "extra": extra or None, "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
 

@@ -56,6 +56,8 @@
 //    32-row blocks that hold rows.
 //  * Each tile's A range ends at its expert's last row: the rows past it
 //    read as zeros through the buffer bound (their results are never stored).
+//    An expert's rows are clamped to [offsets[e], m_cap), so inconsistent
+//    device counts cannot move a read or a write past the buffers.
 //  * Epilogue through LDS: fp32 -> bf16 (SwiGLU for the gated pair) into a
 //    [BM, OUT_N] tile, then 16-byte row-contiguous stores of the valid rows;
 //    a tile larger than the stage buffers goes out in two column passes. The
@@ -95,6 +97,7 @@ struct GemmArgs {
   uint16_t* c;             // [rows, N] bf16 ([rows, 2N] for kSwigluBwd)
   const int32_t* offsets;  // [E_loc + 1]
   const int32_t* counts;   // [E_loc]
+  int64_t m_cap;           // rows of a, c (and aux, aux_out): no row at or past it is touched
   int e_loc;
   int n, k;
   int ldb;                 // row-major b0/b1: row length (K, or k_split for kKSplit)
@@ -200,8 +203,14 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
 #pragma unroll
     for (int q = 0; q < PER; ++q) {
       const int e = tid * PER + q;
-      const int c = e < g.e_loc ? g.counts[e] : 0;
-      if (e < g.e_loc) cnt_s[e] = c, off_s[e] = g.offsets[e];
+      int c = 0;
+      if (e < g.e_loc) {
+        // an expert's rows stay inside [0, m_cap) whatever the device counts say
+        const int o = g.offsets[e];
+        const int64_t room = o < 0 ? 0 : max(int64_t(0), g.m_cap - o);
+        c = int(min(int64_t(max(g.counts[e], 0)), room));
+        cnt_s[e] = c, off_s[e] = o;
+      }
       v[q] = (c + BM - 1) / BM;
       run += v[q];
     }
@@ -591,8 +600,8 @@ hipError_t launch(const GemmArgs& a, hipStream_t s) {
 hipError_t launch_gate_up(const void* x_perm, const int32_t* offsets, const int32_t* counts,
                           int e_loc, int64_t m_cap, int H, int I, const void* w1t,
                           const void* w3t, void* h, hipStream_t s) {
-  (void)m_cap;
   GemmArgs a{};
+  a.m_cap = m_cap;
   a.a = static_cast<const uint16_t*>(x_perm);
   a.b0 = static_cast<const uint16_t*>(w1t);
   a.b1 = static_cast<const uint16_t*>(w3t);
@@ -602,9 +611,10 @@ hipError_t launch_gate_up(const void* x_perm, const int32_t* offsets, const int3
 }
 
 hipError_t launch_gate_up_save(const void* x_perm, const int32_t* offsets, const int32_t* counts,
-                               int e_loc, int H, int I, const void* w1t, const void* w3t, void* h,
-                               void* gu, hipStream_t s) {
+                               int e_loc, int64_t m_cap, int H, int I, const void* w1t,
+                               const void* w3t, void* h, void* gu, hipStream_t s) {
   GemmArgs a{};
+  a.m_cap = m_cap;
   a.a = static_cast<const uint16_t*>(x_perm);
   a.b0 = static_cast<const uint16_t*>(w1t);
   a.b1 = static_cast<const uint16_t*>(w3t);
@@ -616,8 +626,8 @@ hipError_t launch_gate_up_save(const void* x_perm, const int32_t* offsets, const
 
 hipError_t launch_down(const void* h, const int32_t* offsets, const int32_t* counts, int e_loc,
                        int64_t m_cap, int I, int H, const void* w2t, void* y, hipStream_t s) {
-  (void)m_cap;
   GemmArgs a{};
+  a.m_cap = m_cap;
   a.a = static_cast<const uint16_t*>(h);
   a.b0 = static_cast<const uint16_t*>(w2t);
   a.c = static_cast<uint16_t*>(y);
@@ -629,9 +639,10 @@ hipError_t launch_down(const void* h, const int32_t* offsets, const int32_t* cou
 // dh = dy W2^T reads W2 in its math orientation [E_loc, I, H]: for this
 // product that is already output-major (N = I rows of K = H).
 hipError_t launch_down_backward(const void* dy, const void* gu, const int32_t* offsets,
-                                const int32_t* counts, int e_loc, int I, int H, const void* w2,
-                                void* dgu, hipStream_t s) {
+                                const int32_t* counts, int e_loc, int64_t m_cap, int I, int H,
+                                const void* w2, void* dgu, hipStream_t s) {
   GemmArgs a{};
+  a.m_cap = m_cap;
   a.a = static_cast<const uint16_t*>(dy);
   a.b0 = static_cast<const uint16_t*>(w2);
   a.c = static_cast<uint16_t*>(dgu);
@@ -644,9 +655,10 @@ hipError_t launch_down_backward(const void* dy, const void* gu, const int32_t* o
 // dx = [dg | du] [W1 | W3]^T: W1 and W3 in math orientation [E_loc, H, I] are
 // output-major for this product (N = H rows of I), one for each half of K = 2I.
 hipError_t launch_gate_up_backward(const void* dgu, const int32_t* offsets, const int32_t* counts,
-                                   int e_loc, int H, int I, const void* w1, const void* w3,
-                                   void* dx, hipStream_t s) {
+                                   int e_loc, int64_t m_cap, int H, int I, const void* w1,
+                                   const void* w3, void* dx, hipStream_t s) {
   GemmArgs a{};
+  a.m_cap = m_cap;
   a.a = static_cast<const uint16_t*>(dgu);
   a.b0 = static_cast<const uint16_t*>(w1);
   a.b1 = static_cast<const uint16_t*>(w3);

@@ -240,7 +240,7 @@ int32_t moe_grouped_gate_up_save(const void* x_perm_d, const int32_t* offsets_d,
   if (st == MOE_OK && (!gu_d || !aligned16(gu_d))) st = MOE_ERR_ARG;
   if (st != MOE_OK) return st;
   return status_of(moe::launch_gate_up_save(x_perm_d, offsets_d, counts_d, num_local_experts,
-                                            hidden, inter, w1t_d, w3t_d, h_d, gu_d,
+                                            m_cap, hidden, inter, w1t_d, w3t_d, h_d, gu_d,
                                             as_stream(stream)));
 }
 
@@ -253,7 +253,7 @@ int32_t moe_grouped_down_backward(const void* dy_d, const void* gu_d, const int3
   if (st == MOE_OK && (!gu_d || !aligned16(gu_d))) st = MOE_ERR_ARG;
   if (st != MOE_OK) return st;
   return status_of(moe::launch_down_backward(dy_d, gu_d, offsets_d, counts_d, num_local_experts,
-                                             inter, hidden, w2_d, dgu_d, as_stream(stream)));
+                                             m_cap, inter, hidden, w2_d, dgu_d, as_stream(stream)));
 }
 
 int32_t moe_grouped_gate_up_backward(const void* dgu_d, const int32_t* offsets_d,
@@ -265,7 +265,7 @@ int32_t moe_grouped_gate_up_backward(const void* dgu_d, const int32_t* offsets_d
                                 hidden, w1_d, w3_d, dx_perm_d);
   if (st != MOE_OK) return st;
   return status_of(moe::launch_gate_up_backward(dgu_d, offsets_d, counts_d, num_local_experts,
-                                                hidden, inter, w1_d, w3_d, dx_perm_d,
+                                                m_cap, hidden, inter, w1_d, w3_d, dx_perm_d,
                                                 as_stream(stream)));
 }
 
@@ -277,7 +277,7 @@ int32_t moe_grouped_gate_up_wgrad(const void* x_perm_d, const void* dgu_d,
                                 inter, dgu_d, dw1_d, dw3_d);
   if (st != MOE_OK) return st;
   return status_of(moe::launch_gate_up_wgrad(x_perm_d, dgu_d, offsets_d, counts_d,
-                                             num_local_experts, hidden, inter, dw1_d, dw3_d,
+                                             num_local_experts, m_cap, hidden, inter, dw1_d, dw3_d,
                                              as_stream(stream)));
 }
 
@@ -289,7 +289,7 @@ int32_t moe_grouped_down_wgrad(const void* h_d, const void* dy_d, const int32_t*
                                 dy_d, dy_d, dw2_d);
   if (st != MOE_OK) return st;
   return status_of(moe::launch_down_wgrad(h_d, dy_d, offsets_d, counts_d, num_local_experts,
-                                          inter, hidden, dw2_d, as_stream(stream)));
+                                          m_cap, inter, hidden, dw2_d, as_stream(stream)));
 }
 
 int32_t moe_combine(const void* y_d, int64_t y_rows, const int32_t* dst_row_d,

@@ -188,20 +188,20 @@ hipError_t launch_gate_up(const void* x_perm, const int32_t* offsets, const int3
 hipError_t launch_down(const void* h, const int32_t* offsets, const int32_t* counts, int e_loc,
                        int64_t m_cap, int I, int H, const void* w2t, void* y, hipStream_t s);
 hipError_t launch_gate_up_save(const void* x_perm, const int32_t* offsets, const int32_t* counts,
-                               int e_loc, int H, int I, const void* w1t, const void* w3t, void* h,
-                               void* gu, hipStream_t s);
+                               int e_loc, int64_t m_cap, int H, int I, const void* w1t,
+                               const void* w3t, void* h, void* gu, hipStream_t s);
 hipError_t launch_down_backward(const void* dy, const void* gu, const int32_t* offsets,
-                                const int32_t* counts, int e_loc, int I, int H, const void* w2,
-                                void* dgu, hipStream_t s);
+                                const int32_t* counts, int e_loc, int64_t m_cap, int I, int H,
+                                const void* w2, void* dgu, hipStream_t s);
 hipError_t launch_gate_up_backward(const void* dgu, const int32_t* offsets, const int32_t* counts,
-                                   int e_loc, int H, int I, const void* w1, const void* w3,
-                                   void* dx, hipStream_t s);
+                                   int e_loc, int64_t m_cap, int H, int I, const void* w1,
+                                   const void* w3, void* dx, hipStream_t s);
 hipError_t launch_gate_up_wgrad(const void* x_perm, const void* dgu, const int32_t* offsets,
-                                const int32_t* counts, int e_loc, int H, int I, void* dw1,
-                                void* dw3, hipStream_t s);
+                                const int32_t* counts, int e_loc, int64_t m_cap, int H, int I,
+                                void* dw1, void* dw3, hipStream_t s);
 hipError_t launch_down_wgrad(const void* h, const void* dy, const int32_t* offsets,
-                             const int32_t* counts, int e_loc, int I, int H, void* dw2,
-                             hipStream_t s);
+                             const int32_t* counts, int e_loc, int64_t m_cap, int I, int H,
+                             void* dw2, hipStream_t s);
 size_t dispatch_layout_workspace_bytes(int64_t T, int E, int ep);
 hipError_t launch_dispatch_layout(const int32_t* idx, int64_t T, int E, int k, int ep,
                                   int32_t* per_rank, int32_t* per_expert, uint8_t* in_rank,

@@ -48,6 +48,7 @@ struct WgradArgs {
   uint16_t* out1;          // [E_loc, M, N - n_split] bf16 (unused when n_split == N)
   const int32_t* offsets;  // [E_loc + 1]
   const int32_t* counts;   // [E_loc]
+  int64_t m_cap;           // rows of a and b: no row at or past it is read
   int e_loc, m, n, n_split;
 };
 
@@ -102,7 +103,13 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(WgradArgs g) {
       mt = full + r2 % tail;
     }
   };
-  for (int e = threadIdx.x; e < g.e_loc; e += kThreads) cnt_s[e] = g.counts[e], off_s[e] = g.offsets[e];
+  // an expert's rows stay inside [0, m_cap) whatever the device counts say
+  for (int e = threadIdx.x; e < g.e_loc; e += kThreads) {
+    const int o = g.offsets[e];
+    const int64_t room = o < 0 ? 0 : max(int64_t(0), g.m_cap - o);
+    cnt_s[e] = int(min(int64_t(max(g.counts[e], 0)), room));
+    off_s[e] = o;
+  }
   __syncthreads();
   const int total = g.e_loc * per_expert;
   const int G = gridDim.x;
@@ -324,9 +331,10 @@ hipError_t launch_any(const WgradArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_gate_up_wgrad(const void* x_perm, const void* dgu, const int32_t* offsets,
-                                const int32_t* counts, int e_loc, int H, int I, void* dw1,
-                                void* dw3, hipStream_t s) {
+                                const int32_t* counts, int e_loc, int64_t m_cap, int H, int I,
+                                void* dw1, void* dw3, hipStream_t s) {
   WgradArgs a{};
+  a.m_cap = m_cap;
   a.a = static_cast<const uint16_t*>(x_perm);
   a.b = static_cast<const uint16_t*>(dgu);
   a.out0 = static_cast<uint16_t*>(dw1);
@@ -337,9 +345,10 @@ hipError_t launch_gate_up_wgrad(const void* x_perm, const void* dgu, const int32
 }
 
 hipError_t launch_down_wgrad(const void* h, const void* dy, const int32_t* offsets,
-                             const int32_t* counts, int e_loc, int I, int H, void* dw2,
-                             hipStream_t s) {
+                             const int32_t* counts, int e_loc, int64_t m_cap, int I, int H,
+                             void* dw2, hipStream_t s) {
   WgradArgs a{};
+  a.m_cap = m_cap;
   a.a = static_cast<const uint16_t*>(h);
   a.b = static_cast<const uint16_t*>(dy);
   a.out0 = static_cast<uint16_t*>(dw2);

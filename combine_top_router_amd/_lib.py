@@ -40,6 +40,8 @@ SIGNATURES = {
     "moe_layout_workspace_bytes": (_SZ, [C.POINTER(LayoutDesc)]),
     "moe_layout": (_I32, [C.POINTER(LayoutDesc), _P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _P,
                           _SZ, _P]),
+    "moe_layout_noalloc": (_I32, [C.POINTER(LayoutDesc), _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                  _I64, _P]),
     "moe_dispatch_layout_workspace_bytes": (_SZ, [_I64, _I32, _I32, _I32]),
     "moe_dispatch_layout": (_I32, [_P, _I64, _I32, _I32, _I32, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_permute": (_I32, [_P, _I64, _I32, _I32, _P, _I64, _P, _P]),

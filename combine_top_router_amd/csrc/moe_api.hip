@@ -5,6 +5,7 @@
 #include <algorithm>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "../../include/moe.h"
@@ -78,6 +79,7 @@ const char* moe_status_string(int32_t status) {
     case MOE_ERR_COVERAGE: return "MOE_ERR_COVERAGE";
     case MOE_ERR_EXPERT_ID: return "MOE_ERR_EXPERT_ID";
     case MOE_ERR_LAYOUT: return "MOE_ERR_LAYOUT";
+    case MOE_ERR_TOO_LARGE: return "MOE_ERR_TOO_LARGE";
     default: return "MOE_ERR_UNKNOWN";
   }
 }
@@ -104,21 +106,84 @@ size_t moe_layout_workspace_bytes(const moe_layout_desc* desc) {
   return desc_ok(desc) ? moe::layout_workspace_bytes(plan_of(desc)) : 0;
 }
 
+}  // extern "C"
+
+namespace {
+
+// moe_layout's checks of everything but the workspace
+int32_t layout_args(const moe_layout_desc* desc, const int32_t* topk_idx_d,
+                    const int32_t* offsets_d, const int32_t* dst_row_d, const int32_t* src_row_d,
+                    int64_t m_cap) {
+  if (!desc_ok(desc)) return MOE_ERR_ARG;
+  if (!offsets_d || !src_row_d) return MOE_ERR_ARG;
+  if (desc->num_tokens > 0 && (!topk_idx_d || !dst_row_d)) return MOE_ERR_ARG;
+  if (m_cap < m_cap_of(desc) || m_cap > (int64_t(1) << 31) - 1) return MOE_ERR_ARG;
+  return MOE_OK;
+}
+
+// The layout's workspace for callers that cannot allocate: a static device
+// array of MOE_LAYOUT_SCRATCH_BYTES. Each GPU the library runs on holds its
+// own copy, at its own address, until the process ends. In host code
+// `scratch` names a host-side stand-in, never the device memory: the device
+// address of each GPU's copy comes from hipGetSymbolAddress, looked up once
+// per device with that device current, and only that address reaches a
+// kernel. Nothing in the layout's workspace needs to start at zero: every
+// word is written before it is read in the same call.
+static __device__ __align__(256) char scratch[MOE_LAYOUT_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_dev[kMaxDevices];  // device address of each GPU's copy, once looked up
+
+int32_t scratch_of_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_dev[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_ERR_HIP;
+    scratch_dev[dev] = p;
+  }
+  *out = scratch_dev[dev];
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 int32_t moe_layout(const moe_layout_desc* desc, const int32_t* topk_idx_d,
                    int32_t* expert_counts_d, int32_t* send_counts_d, int32_t* split_matrix_d,
                    int32_t* recv_counts_d, int32_t* output_splits_d, int32_t* offsets_d,
                    int32_t* dst_row_d, int32_t* src_row_d, int64_t m_cap, void* workspace_d,
                    size_t workspace_bytes, void* stream) {
-  if (!desc_ok(desc)) return MOE_ERR_ARG;
-  if (!offsets_d || !src_row_d || !workspace_d || !aligned16(workspace_d)) return MOE_ERR_ARG;
-  if (desc->num_tokens > 0 && (!topk_idx_d || !dst_row_d)) return MOE_ERR_ARG;
-  if (m_cap < m_cap_of(desc) || m_cap > (int64_t(1) << 31) - 1) return MOE_ERR_ARG;
+  const int32_t st = layout_args(desc, topk_idx_d, offsets_d, dst_row_d, src_row_d, m_cap);
+  if (st != MOE_OK) return st;
+  if (!workspace_d || !aligned16(workspace_d)) return MOE_ERR_ARG;
   const moe::LayoutPlan p = plan_of(desc);
   if (workspace_bytes < moe::layout_workspace_bytes(p)) return MOE_ERR_ARG;
   return status_of(moe::launch_layout(p, topk_idx_d, expert_counts_d, send_counts_d,
                                       split_matrix_d, recv_counts_d, output_splits_d, offsets_d,
                                       dst_row_d, src_row_d, m_cap, workspace_d,
                                       as_stream(stream)));
+}
+
+int32_t moe_layout_noalloc(const moe_layout_desc* desc, const int32_t* topk_idx_d,
+                           int32_t* expert_counts_d, int32_t* send_counts_d,
+                           int32_t* split_matrix_d, int32_t* recv_counts_d,
+                           int32_t* output_splits_d, int32_t* offsets_d, int32_t* dst_row_d,
+                           int32_t* src_row_d, int64_t m_cap, void* stream) {
+  int32_t st = layout_args(desc, topk_idx_d, offsets_d, dst_row_d, src_row_d, m_cap);
+  if (st != MOE_OK) return st;
+  const moe::LayoutPlan p = plan_of(desc);
+  if (moe::layout_workspace_bytes(p) > MOE_LAYOUT_SCRATCH_BYTES) return MOE_ERR_TOO_LARGE;
+  void* ws = nullptr;
+  st = scratch_of_current_device(&ws);
+  if (st != MOE_OK) return st;
+  return status_of(moe::launch_layout(p, topk_idx_d, expert_counts_d, send_counts_d,
+                                      split_matrix_d, recv_counts_d, output_splits_d, offsets_d,
+                                      dst_row_d, src_row_d, m_cap, ws, as_stream(stream)));
 }
 
 static bool dl_args_ok(int64_t T, int32_t E, int32_t k, int32_t ep) {

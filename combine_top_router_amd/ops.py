@@ -94,7 +94,7 @@ class Layout:
         return self.expert_counts[self.first_local:self.first_local + self.num_local]
 
 
-def alloc_layout(desc: LayoutDesc, device, m_cap=None) -> Layout:
+def alloc_layout(desc: LayoutDesc, device, m_cap=None, workspace: bool = True) -> Layout:
     T, E, k, ep = desc.num_tokens, desc.num_experts, desc.top_k, desc.ep_size
     first = 0 if desc.local_rank < 0 else desc.local_rank * (E // ep)
     el = E if desc.local_rank < 0 else E // ep
@@ -105,7 +105,8 @@ def alloc_layout(desc: LayoutDesc, device, m_cap=None) -> Layout:
                   _empty((ep, ep), i32, device), _empty((ep, el), i32, device),
                   _empty((ep,), i32, device), _empty((el + 1,), i32, device),
                   _empty((T, k), i32, device), _empty((m_cap,), i32, device),
-                  _empty((max(layout_workspace_bytes(desc), 16),), torch.uint8, device))
+                  _empty((max(layout_workspace_bytes(desc) if workspace else 0, 16),),
+                         torch.uint8, device))
 
 
 def layout(topk_idx: torch.Tensor, num_experts: int, ep_size: int = 1, local_rank: int = -1,
@@ -120,6 +121,22 @@ def layout(topk_idx: torch.Tensor, num_experts: int, ep_size: int = 1, local_ran
         _ptr(L.split_matrix), _ptr(L.recv_counts), _ptr(L.output_splits), _ptr(L.offsets),
         _ptr(L.dst_row), _ptr(L.src_row), L.m_cap, _ptr(L.workspace), L.workspace.numel(),
         _stream(topk_idx.device)))
+    return L
+
+
+def layout_noalloc(topk_idx: torch.Tensor, num_experts: int, ep_size: int = 1,
+                   local_rank: int = -1, align: int = 128, out: Layout | None = None) -> Layout:
+    """As ``layout``, through moe_layout_noalloc: the library's static scratch
+    array serves as the workspace, so the call allocates nothing (``out``,
+    when given, holds every output; its workspace is not used)."""
+    _need(topk_idx, "topk_idx", torch.int32)
+    T, k = topk_idx.shape
+    desc = layout_desc(T, num_experts, k, ep_size, local_rank, align)
+    L = alloc_layout(desc, topk_idx.device, workspace=False) if out is None else out
+    check("moe_layout_noalloc", lib().moe_layout_noalloc(
+        C.byref(desc), _ptr(topk_idx), _ptr(L.expert_counts), _ptr(L.send_counts),
+        _ptr(L.split_matrix), _ptr(L.recv_counts), _ptr(L.output_splits), _ptr(L.offsets),
+        _ptr(L.dst_row), _ptr(L.src_row), L.m_cap, _stream(topk_idx.device)))
     return L
 
 

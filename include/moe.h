@@ -10,6 +10,8 @@
  *   device; descriptors (moe_layout_desc) are HOST memory. The caller owns
  *   and allocates every buffer; the library allocates nothing, keeps no state
  *   between calls and never blocks the host (moe_validate_layout excepted).
+ *   The one exception to the ownership rule is moe_layout_noalloc, whose
+ *   workspace is a static device array of the library (one per GPU).
  * - `stream` is a hipStream_t (NULL = the default stream). Each call only
  *   enqueues kernels on it and returns; results are ready when the stream
  *   reaches that point. Calls on different streams may run concurrently as
@@ -41,7 +43,9 @@ typedef enum moe_status {
   MOE_ERR_HIP = 3,          /* a HIP runtime call or kernel launch failed */
   MOE_ERR_COVERAGE = 4,     /* validator: a (token, slot) is missing or covered twice */
   MOE_ERR_EXPERT_ID = 5,    /* validator: expert id out of range or repeated in a token */
-  MOE_ERR_LAYOUT = 6        /* validator: offsets / src_row / dst_row inconsistent */
+  MOE_ERR_LAYOUT = 6,       /* validator: offsets / src_row / dst_row inconsistent */
+  MOE_ERR_TOO_LARGE = 7     /* moe_layout_noalloc: the layout needs more scratch than the
+                               library's static array holds */
 } moe_status;
 
 /* Static name of a status code ("MOE_OK", ...); never NULL. */
@@ -134,6 +138,30 @@ int32_t moe_layout(const moe_layout_desc* desc, const int32_t* topk_idx_d,
                    int32_t* output_splits_d, int32_t* offsets_d, int32_t* dst_row_d,
                    int32_t* src_row_d, int64_t m_cap, void* workspace_d,
                    size_t workspace_bytes, void* stream);
+
+/*
+ * moe_layout_noalloc -- moe_layout for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): no workspace argument, and the call allocates nothing.
+ * The workspace lives in a static device array of MOE_LAYOUT_SCRATCH_BYTES
+ * (4 MiB) that each GPU the library runs on holds until the process ends;
+ * its device address is looked up once per device, on the first call with
+ * that device current. Outputs, arguments and results are those of
+ * moe_layout (the same kernels), on the current device's stream `stream`.
+ * Limit: moe_layout_workspace_bytes(desc) <= MOE_LAYOUT_SCRATCH_BYTES, else
+ * MOE_ERR_TOO_LARGE and nothing is launched (at 256 experts, up to about 16 M
+ * assignments T * top_k). Every call on one GPU shares that GPU's array:
+ * calls that overlap on one GPU (on two streams, or from two host threads
+ * without ordering) race and must not be made. Nothing in the array needs to
+ * start at zero; a call leaves its contents behind.
+ */
+#define MOE_LAYOUT_SCRATCH_BYTES (4u << 20)
+
+int32_t moe_layout_noalloc(const moe_layout_desc* desc, const int32_t* topk_idx_d,
+                           int32_t* expert_counts_d, int32_t* send_counts_d,
+                           int32_t* split_matrix_d, int32_t* recv_counts_d,
+                           int32_t* output_splits_d, int32_t* offsets_d, int32_t* dst_row_d,
+                           int32_t* src_row_d, int64_t m_cap, void* stream);
 
 /*
  * moe_dispatch_layout -- per-rank deduplicated dispatch layout.

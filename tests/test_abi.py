@@ -109,3 +109,22 @@ def test_argument_checks_return_before_launch(lib):
     assert lib.moe_pack_weights(fake, 2, 4, 4, fake, None) == 1                 # in place
     assert lib.moe_pack_weights(fake, 2, 64, 128, odd, None) == 2               # K % 128
     assert lib.moe_pack_weights(fake, 2, 128, 192, odd, None) == 2              # N % 128
+
+
+def test_noalloc_layout_rejects_work_past_its_static_scratch(lib):
+    # 2^20 tokens, top-16 of 1024 experts: 2048 layout tiles of 8192 assignments,
+    # 8 MiB of per-tile histograms, past the 4 MiB static array; refused on the
+    # host, before any device call
+    T, E, k = 1 << 20, 1024, 16
+    d = _desc(T, E, k, 1, -1, 1)
+    assert lib.moe_layout_workspace_bytes(C.byref(d)) > 4 << 20
+    m_cap = lib.moe_layout_m_cap(C.byref(d))
+    fake = C.c_void_p(1 << 20)
+    st = lib.moe_layout_noalloc(C.byref(d), fake, fake, fake, fake, fake, fake, fake, fake, fake,
+                                m_cap, None)
+    assert st == 7 and lib.moe_status_string(st) == b"MOE_ERR_TOO_LARGE"
+    # the checks moe_layout makes come first
+    assert lib.moe_layout_noalloc(C.byref(d), fake, fake, fake, fake, fake, fake, fake, fake,
+                                  fake, m_cap - 1, None) == 1
+    assert lib.moe_layout_noalloc(C.byref(_desc(64, 8, 2)), fake, fake, fake, fake, fake, fake,
+                                  None, fake, fake, 2000, None) == 1

@@ -64,6 +64,9 @@ def parse():
                          "read and written before every stage, outside its events)")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for the CPU baseline sample")
+    ap.add_argument("--layout-sweep", action="store_true",
+                    help="only time the layout stage alone from 64 K to 64 M assignments "
+                         "(256 experts, top-8, all local) and exit")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB five times (the reference "
                          "kernel for scaling rocprofv3 FETCH_SIZE/WRITE_SIZE readings) and exit")
@@ -469,10 +472,57 @@ def combine_only(cfg, args, dev, flush):
     return rec
 
 
+def layout_sweep(args):
+    """The layout stage on its own at growing sizes: T*8 assignments over 256
+    experts (top-8, softmax routing of N(0, 1) logits, every expert local,
+    alignment 128), 64 K to 64 M assignments. Each point: the mean of 20 calls
+    back to back, priced on the layout's algorithmic bytes (the expert ids
+    read once, dst_row and src_row written once)."""
+    import numpy as np
+    import torch
+
+    import combine_top_router_amd as moe
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    E, k, reps = 256, 8, 20
+    points = []
+    for n in [1 << p for p in range(16, 27, 2)]:
+        T = n // k
+        g = torch.Generator(device=dev)
+        g.manual_seed(n)
+        logits = torch.randn((T, E), generator=g, device=dev)
+        idx, _ = moe.route(logits, k)
+        del logits
+        L = moe.layout(idx, E, 1, -1, 128)
+        for _ in range(3):
+            moe.layout(idx, E, 1, -1, 128, out=L)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        ev[0].record(stream)
+        for r in range(reps):
+            moe.layout(idx, E, 1, -1, 128, out=L)
+            ev[r + 1].record(stream)
+        torch.cuda.synchronize()
+        ms = float(np.mean([ev[r].elapsed_time(ev[r + 1]) for r in range(reps)]))
+        nbytes = n * 4 * 2 + n * 4
+        points.append({"assignments": n, "tokens": T, "us": round(ms * 1e3, 2),
+                       "bytes": nbytes, "GB/s": round(nbytes / ms / 1e6, 1),
+                       "frac": round(nbytes / ms / 1e6 / PEAK_HBM_GBS, 4)})
+        log(f"layout {n} assignments: {ms * 1e3:.1f} us")
+        del idx, L
+        torch.cuda.empty_cache()
+    print(json.dumps({"layout_sweep": points, "experts": E, "top_k": k, "align": 128}),
+          flush=True)
+
+
 def main():
     args = parse()
     if args.calibrate_copy:
         calibrate_copy(args.calibrate_copy)
+        return
+    if args.layout_sweep:
+        layout_sweep(args)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): it measures one "

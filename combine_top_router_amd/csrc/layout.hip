@@ -13,19 +13,28 @@
 // token*top_k + slot (DeepSpeed PR #8847, section "Change").
 //
 // Up to 4096 assignments one workgroup does everything in one launch (see
-// layout_fused_kernel): one CU is then as fast as the whole chip and two
-// launches are saved. Beyond that, three kernels on one stream:
+// layout_fused_kernel): one CU is then as fast as the whole chip. Beyond that,
+// two kernels on one stream:
 //   count   one workgroup per tile of flat assignments (tiles never cross a
-//           source-rank boundary): LDS histogram over all experts.
-//   scan    one workgroup: per-rank and per-expert totals, split matrix,
-//           receive counts, padded offsets, and each tile's exclusive base
-//           row per local expert.
-//   scatter one workgroup per tile: ranks inside the tile from wavefront
-//           ballots (lanes holding the same local expert find each other
-//           with key_bits ballots, then popcount below their lane), in
+//           source-rank boundary): LDS histogram over all experts, written
+//           out.
+//   place   one workgroup per tile and one more. Each derives from the tile
+//           histograms alone what its tile needs: every local expert's total
+//           and padded offset, and the rows the earlier tiles hold; the extra
+//           workgroup writes the split plan (per-rank and per-expert totals,
+//           split matrix, receive counts). Then ranks inside the tile from
+//           wavefront ballots (lanes holding the same local expert find each
+//           other with key_bits ballots, then popcount below their lane), in
 //           flat-index order, so the permutation is stable and does not
-//           depend on scheduling; writes dst_row and src_row, then marks the
-//           padding and tail rows of src_row with -1.
+//           depend on scheduling; dst_row and src_row are written, and the
+//           padding and tail rows of src_row get -1.
+// No workgroup waits for or reads from another inside a launch: placing a row
+// needs the totals of every tile, and a grid-wide wait would need a launch
+// that guarantees every workgroup is resident, while exchanging data between
+// workgroups of one launch costs a device-scope fence, which on this chip
+// writes back and invalidates the whole L2 of the XCD. Tiles grow with the
+// assignment count (128 to 256 of them), so the histograms each placing
+// workgroup reads stay small.
 #include <algorithm>
 
 #include "moe_internal.h"
@@ -33,49 +42,16 @@
 namespace moe {
 namespace {
 
-constexpr int kThreads = 256;
-
-struct Ws {
-  int32_t* tile_hist;  // [num_tiles, E]
-  int32_t* tile_base;  // [num_tiles, e_loc]
-  int32_t* lcount;     // [e_loc]
-};
+constexpr int kThreads = 1024;  // 16 wavefronts, both kernels of the tiled path
+constexpr int kWavesPerGroup = kThreads / kWave;
 
 __host__ __device__ inline size_t round256(size_t b) { return (b + 255) & ~size_t(255); }
-
-Ws carve(const LayoutPlan& p, void* base) {
-  char* c = static_cast<char*>(base);
-  Ws w;
-  w.tile_hist = reinterpret_cast<int32_t*>(c);
-  c += round256(sizeof(int32_t) * size_t(p.num_tiles) * p.E);
-  w.tile_base = reinterpret_cast<int32_t*>(c);
-  c += round256(sizeof(int32_t) * size_t(p.num_tiles) * p.e_loc);
-  w.lcount = reinterpret_cast<int32_t*>(c);
-  return w;
-}
 
 __device__ __forceinline__ void tile_range(const LayoutPlan& p, int b, int64_t& start,
                                            int64_t& end) {
   const int s = b / p.tiles_per_rank, j = b % p.tiles_per_rank;
   start = s * p.chunk + int64_t(j) * p.tile;
   end = min(start + p.tile, int64_t(s + 1) * p.chunk);
-}
-
-__global__ __launch_bounds__(kThreads) void layout_count_kernel(LayoutPlan p,
-                                                                const int32_t* __restrict__ idx,
-                                                                int32_t* __restrict__ tile_hist) {
-  extern __shared__ int32_t hist[];  // [E]
-  const int b = blockIdx.x;
-  for (int e = threadIdx.x; e < p.E; e += kThreads) hist[e] = 0;
-  __syncthreads();
-  int64_t start, end;
-  tile_range(p, b, start, end);
-  for (int64_t i = start + threadIdx.x; i < end; i += kThreads) {
-    const int e = idx[i];
-    if (static_cast<unsigned>(e) < static_cast<unsigned>(p.E)) atomicAdd(&hist[e], 1);
-  }
-  __syncthreads();
-  for (int e = threadIdx.x; e < p.E; e += kThreads) tile_hist[size_t(b) * p.E + e] = hist[e];
 }
 
 // Inclusive scan over a workgroup of 1024 threads (16 wavefronts).
@@ -100,163 +76,268 @@ __device__ int block_inclusive_scan_1024(int v, int* wave_tot) {
   return v + wave_tot[w];
 }
 
-__global__ __launch_bounds__(1024) void layout_scan_kernel(
-    LayoutPlan p, const int32_t* __restrict__ tile_hist, int32_t* __restrict__ tile_base,
-    int32_t* __restrict__ lcount_ws, int32_t* __restrict__ expert_counts,
-    int32_t* __restrict__ send_counts, int32_t* __restrict__ split_matrix,
-    int32_t* __restrict__ recv_counts, int32_t* __restrict__ output_splits,
-    int32_t* __restrict__ offsets) {
-  extern __shared__ int32_t sm[];
-  int32_t* send = sm;                      // [ep, E]
-  int32_t* lcount = send + p.ep * p.E;     // [e_loc]
-  int32_t* wave_tot = lcount + p.e_loc;    // [16]
-  const int tpr = p.tiles_per_rank;
+// As batched_run with NB loads in flight per batch: i = i0 .. i1-1, every
+// load(i) of a batch issued before the batch's values are used, in order.
+template <int NB, class L, class U>
+__device__ __forceinline__ void batched_run_n(int i0, int i1, L&& load, U&& use) {
+  for (int i = i0; i < i1; i += NB) {
+    int v[NB];
+#pragma unroll
+    for (int u = 0; u < NB; ++u) v[u] = i + u < i1 ? load(i + u) : 0;
+#pragma unroll
+    for (int u = 0; u < NB; ++u)
+      if (i + u < i1) use(i + u, v[u]);
+  }
+}
 
-  for (int e = threadIdx.x; e < p.E; e += 1024) {
-    const bool loc = e >= p.first && e < p.first + p.e_loc;
-    const int el = e - p.first;
-    int total = 0;
-    for (int s = 0; s < p.ep; ++s) {
-      int rs = 0;
-      int j = 0;
-      for (; j + 4 <= tpr; j += 4) {  // four independent loads in flight
-        const int b = s * tpr + j;
-        int c[4];
+// One workgroup per tile of flat assignments (tiles never cross a
+// source-rank boundary): LDS histogram over all experts, written out. Each
+// thread's expert ids are loaded eight at a time before any is counted.
+__global__ __launch_bounds__(kThreads) void layout_count_kernel(LayoutPlan p,
+                                                                const int32_t* __restrict__ idx,
+                                                                int32_t* __restrict__ tile_hist) {
+  extern __shared__ int32_t hist[];  // [E]
+  const int b = blockIdx.x;
+  for (int e = threadIdx.x; e < p.E; e += kThreads) hist[e] = 0;
+  __syncthreads();
+  int64_t start, end;
+  tile_range(p, b, start, end);
+  for (int64_t i0 = start + threadIdx.x; i0 < end; i0 += 8 * int64_t(kThreads)) {
+    int ev[8];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) c[u] = tile_hist[size_t(b + u) * p.E + e];
+    for (int u = 0; u < 8; ++u) {
+      const int64_t i = i0 + int64_t(u) * kThreads;
+      ev[u] = i < end ? idx[i] : -1;
+    }
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          if (loc) tile_base[size_t(b + u) * p.e_loc + el] = total + rs;
-          rs += c[u];
-        }
-      }
-      for (; j < tpr; ++j) {
-        const int b = s * tpr + j;
-        const int c = tile_hist[size_t(b) * p.E + e];
-        if (loc) tile_base[size_t(b) * p.e_loc + el] = total + rs;
-        rs += c;
-      }
-      send[s * p.E + e] = rs;
-      if (send_counts) send_counts[s * p.E + e] = rs;
-      total += rs;
-    }
-    if (expert_counts) expert_counts[e] = total;
-    if (loc) {
-      lcount[el] = total;
-      lcount_ws[el] = total;
-    }
+    for (int u = 0; u < 8; ++u)
+      if (static_cast<unsigned>(ev[u]) < static_cast<unsigned>(p.E)) atomicAdd(&hist[ev[u]], 1);
   }
   __syncthreads();
+  for (int e = threadIdx.x; e < p.E; e += kThreads) tile_hist[size_t(b) * p.E + e] = hist[e];
+}
 
+// The split plan (per-rank and per-expert totals, split matrix, receive
+// counts, output splits) from the tile histograms, by the one workgroup past
+// the tiles of the place kernel. Thread (g, e), g < 1024 / E, sums a run of
+// tile rows of expert e, source rank by source rank, into LDS.
+__device__ void layout_split_plan(const LayoutPlan& p, const int32_t* __restrict__ tile_hist,
+                                  int32_t* __restrict__ expert_counts,
+                                  int32_t* __restrict__ send_counts,
+                                  int32_t* __restrict__ split_matrix,
+                                  int32_t* __restrict__ recv_counts,
+                                  int32_t* __restrict__ output_splits, int32_t* send) {
+  const int tid = threadIdx.x, E = p.E, el_n = p.e_loc, nt = p.num_tiles;
+  for (int q = tid; q < p.ep * E; q += kThreads) send[q] = 0;
+  __syncthreads();
+  const int G = kThreads / E, e = tid % E, g = tid / E;
+  if (g < G) {
+    const int per = (nt + G - 1) / G, b0 = min(nt, g * per), b1 = min(nt, b0 + per);
+    int rank_sum = 0, cur = b0 < b1 ? b0 / p.tiles_per_rank : 0;
+    batched_run_n<32>(b0, b1, [&](int b) { return tile_hist[size_t(b) * E + e]; }, [&](int b, int v) {
+      const int s = b / p.tiles_per_rank;
+      if (s != cur) {
+        atomicAdd(&send[cur * E + e], rank_sum);
+        rank_sum = 0;
+        cur = s;
+      }
+      rank_sum += v;
+    });
+    if (b0 < b1) atomicAdd(&send[cur * E + e], rank_sum);
+  }
+  __syncthreads();
+  if (send_counts)
+    for (int q = tid; q < p.ep * E; q += kThreads) send_counts[q] = send[q];
+  if (expert_counts)
+    for (int e2 = tid; e2 < E; e2 += kThreads) {
+      int t = 0;
+      for (int s = 0; s < p.ep; ++s) t += send[s * E + e2];
+      expert_counts[e2] = t;
+    }
   if (recv_counts)
-    for (int q = threadIdx.x; q < p.ep * p.e_loc; q += 1024)
-      recv_counts[q] = send[(q / p.e_loc) * p.E + p.first + q % p.e_loc];
+    for (int q = tid; q < p.ep * el_n; q += kThreads)
+      recv_counts[q] = send[(q / el_n) * E + p.first + q % el_n];
   if (output_splits)
-    for (int s = threadIdx.x; s < p.ep; s += 1024) {
+    for (int s = tid; s < p.ep; s += kThreads) {
       int sum = 0;
-      for (int el = 0; el < p.e_loc; ++el) sum += send[s * p.E + p.first + el];
+      for (int el = 0; el < el_n; ++el) sum += send[s * E + p.first + el];
       output_splits[s] = sum;
     }
   if (split_matrix) {
-    const int eper = p.E / p.ep;
-    for (int q = threadIdx.x; q < p.ep * p.ep; q += 1024) {
+    const int eper = E / p.ep;
+    for (int q = tid; q < p.ep * p.ep; q += kThreads) {
       const int s = q / p.ep, d = q % p.ep;
       int sum = 0;
-      for (int e = 0; e < eper; ++e) sum += send[s * p.E + d * eper + e];
+      for (int e2 = 0; e2 < eper; ++e2) sum += send[s * E + d * eper + e2];
       split_matrix[q] = sum;
     }
   }
-
-  // padded offsets over local experts (e_loc <= 1024)
-  int padded = 0;
-  if (threadIdx.x < p.e_loc) {
-    const int c = lcount[threadIdx.x];
-    padded = (c + p.align - 1) / p.align * p.align;
-  }
-  const int incl = block_inclusive_scan_1024(padded, wave_tot);
-  if (threadIdx.x == 0) offsets[0] = 0;
-  if (threadIdx.x < p.e_loc) offsets[threadIdx.x + 1] = incl;
 }
 
+// One workgroup per tile, plus one for the split plan. Each first derives,
+// from the tile histograms alone, every local expert's total and padded
+// offset and the rows its tile's predecessors hold (thread (g, el) sums a run
+// of tile rows; the tile histograms are small and stay in L2), so no
+// workgroup depends on another. Then the tile's rows: ranks inside the tile
+// from wavefront ballots (lanes holding the same local expert find each other
+// with key_bits ballots, then popcount below their lane), in flat-index
+// order, so the permutation is stable and does not depend on scheduling; a
+// tile of more than 1024 * R assignments is walked in passes of that many,
+// each expert's next row carried from pass to pass. Last, the padding and
+// tail rows of src_row get -1.
 template <int R>
-__global__ __launch_bounds__(kThreads) void layout_scatter_kernel(
-    LayoutPlan p, const int32_t* __restrict__ idx, const int32_t* __restrict__ tile_base,
-    const int32_t* __restrict__ lcount, const int32_t* __restrict__ offsets,
+__global__ __launch_bounds__(kThreads) void layout_place_kernel(
+    LayoutPlan p, const int32_t* __restrict__ idx, const int32_t* __restrict__ tile_hist,
+    int32_t* __restrict__ expert_counts, int32_t* __restrict__ send_counts,
+    int32_t* __restrict__ split_matrix, int32_t* __restrict__ recv_counts,
+    int32_t* __restrict__ output_splits, int32_t* __restrict__ offsets,
     int32_t* __restrict__ dst_row, int32_t* __restrict__ src_row, int64_t m_cap) {
   extern __shared__ int32_t sm[];
-  const int el_n = p.e_loc;
-  int32_t* cnt = sm;               // [4, e_loc]: running count per wavefront
-  int32_t* wbase = sm + 4 * el_n;  // [4, e_loc]: exclusive prefix over wavefronts
-  const int b = blockIdx.x;
-  const int w = threadIdx.x / kWave, lane = lane_id();
+  const int el_n = p.e_loc, nt = p.num_tiles, b = blockIdx.x;
+  const int w = threadIdx.x / kWave, lane = lane_id(), tid = threadIdx.x;
+  if (b == nt) {  // the split plan, in its own workgroup, and nothing else
+    layout_split_plan(p, tile_hist, expert_counts, send_counts, split_matrix, recv_counts,
+                      output_splits, sm);
+    return;
+  }
+  const int G = kThreads / el_n;                // runs of tile rows per expert (>= 1)
+  // LDS: the run sums [2, G, e_loc] of the offset pass, then the per-wavefront
+  // counts [16, e_loc] in the same words; after both, base, offsets, totals
+  const int head = max(kWavesPerGroup * el_n, 2 * G * el_n);
+  int32_t* part = sm;
+  int32_t* cnt = sm;
+  int32_t* base = sm + head;                    // [e_loc]: the next row of each local expert
+  int32_t* off = base + el_n;                   // [e_loc + 1]: padded offsets
+  int32_t* total = off + el_n + 1;              // [e_loc]
+  int32_t* wave_tot = total + el_n;             // [16]
 
-  if (b < p.num_tiles) {
-    for (int q = threadIdx.x; q < 4 * el_n; q += kThreads) cnt[q] = 0;
-    __syncthreads();
-
-    int64_t start, end;
-    tile_range(p, b, start, end);
-    const int64_t sub_start = start + int64_t(w) * (kWave * R);
+  // this wavefront's expert ids of a pass, loaded a pass ahead; the first
+  // pass's go out now, so they arrive while the offsets are derived
+  int64_t start, end;
+  tile_range(p, b, start, end);
+  auto load_ids = [&](int64_t pass, int (&ev)[R]) {
+    const int64_t sub_start = pass + int64_t(w) * (kWave * R);
     const int64_t sub_end = min(sub_start + kWave * R, end);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int64_t i = sub_start + kWave * r + lane;
+      ev[r] = i < sub_end ? idx[i] : -1;
+    }
+  };
+  int nxt[R];
+  load_ids(start, nxt);
+
+  // totals, padded offsets and this tile's first row of each local expert
+  {
+    const int el = tid % el_n, g = tid / el_n;
+    if (g < G) {
+      const int per = (nt + G - 1) / G, b0 = min(nt, g * per), b1 = min(nt, b0 + per);
+      const int32_t* col = tile_hist + p.first + el;
+      int tot = 0, before = 0;
+      batched_run_n<32>(b0, b1, [&](int bb) { return col[size_t(bb) * p.E]; }, [&](int bb, int v) {
+        tot += v;
+        if (bb < b) before += v;
+      });
+      part[g * el_n + el] = tot;
+      part[(G + g) * el_n + el] = before;
+    }
+    __syncthreads();
+    int padded = 0, before = 0;
+    if (tid < el_n) {
+      int t = 0;
+      for (int g2 = 0; g2 < G; ++g2) {
+        t += part[g2 * el_n + tid];
+        before += part[(G + g2) * el_n + tid];
+      }
+      total[tid] = t;
+      padded = (t + p.align - 1) / p.align * p.align;
+    }
+    const int incl = block_inclusive_scan_1024(padded, wave_tot);
+    if (tid == 0) off[0] = 0;
+    if (tid < el_n) {
+      off[tid + 1] = incl;
+      base[tid] = incl - padded + before;
+    }
+    if (b == 0) {
+      if (tid == 0) offsets[0] = 0;
+      if (tid < el_n) offsets[tid + 1] = incl;
+    }
+    __syncthreads();
+  }
+
+  {
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
 
-    int key[R], pre[R];
+    for (int64_t pass = start; pass < end; pass += int64_t(kThreads) * R) {
+      int ev[R];
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int64_t i = sub_start + kWave * r + lane;
-      const bool valid = i < sub_end;
-      const int e = valid ? idx[i] : -1;
-      const int el = (e >= p.first && e < p.first + el_n) ? e - p.first : el_n;
-      key[r] = el;
-      // lanes holding the same key: intersect ballots of each key bit
-      uint64_t m = __ballot(valid);
-      for (int bit = 0; bit < p.key_bits; ++bit) {
-        const bool set = (el >> bit) & 1;
-        const uint64_t bb = __ballot(set);
-        m &= set ? bb : ~bb;
-      }
-      pre[r] = 0;
-      if (el < el_n) {
-        const int old = cnt[w * el_n + el];
-        const int rank = __popcll(m & below);
-        pre[r] = old + rank;
-        if (rank == 0) cnt[w * el_n + el] = old + __popcll(m);
-      }
-    }
-    __syncthreads();
-    for (int el = threadIdx.x; el < el_n; el += kThreads) {
-      int run = 0;
+      for (int r = 0; r < R; ++r) ev[r] = nxt[r];
+      if (pass + int64_t(kThreads) * R < end) load_ids(pass + int64_t(kThreads) * R, nxt);
+      for (int q = tid; q < kWavesPerGroup * el_n; q += kThreads) cnt[q] = 0;
+      __syncthreads();
+      const int64_t sub_start = pass + int64_t(w) * (kWave * R);
+      const int64_t sub_end = min(sub_start + kWave * R, end);
+
+      int key[R], pre[R];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        wbase[q * el_n + el] = run;
-        run += cnt[q * el_n + el];
+      for (int r = 0; r < R; ++r) {
+        const int64_t i = sub_start + kWave * r + lane;
+        const bool valid = i < sub_end;
+        const int e = ev[r];
+        const int el = (e >= p.first && e < p.first + el_n) ? e - p.first : el_n;
+        key[r] = el;
+        // lanes holding the same key: intersect ballots of each key bit
+        uint64_t m = __ballot(valid);
+        for (int bit = 0; bit < p.key_bits; ++bit) {
+          const bool set = (el >> bit) & 1;
+          const uint64_t bb = __ballot(set);
+          m &= set ? bb : ~bb;
+        }
+        pre[r] = 0;
+        if (valid && el < el_n) {
+          const int old = cnt[w * el_n + el];
+          const int rank = __popcll(m & below);
+          pre[r] = old + rank;
+          if (rank == 0) cnt[w * el_n + el] = old + __popcll(m);
+        }
       }
-    }
-    __syncthreads();
+      __syncthreads();
+      // exclusive prefix over the wavefronts, per local expert, from the
+      // expert's next row; the total moves that row on for the next pass
+      for (int el = tid; el < el_n; el += kThreads) {
+        int run = base[el];
+        for (int q = 0; q < kWavesPerGroup; ++q) {
+          const int c = cnt[q * el_n + el];
+          cnt[q * el_n + el] = run;
+          run += c;
+        }
+        base[el] = run;
+      }
+      __syncthreads();
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int64_t i = sub_start + kWave * r + lane;
-      if (i >= sub_end) continue;
-      const int el = key[r];
-      if (el < el_n) {
-        const int64_t row = int64_t(offsets[el]) + tile_base[size_t(b) * el_n + el] +
-                            wbase[w * el_n + el] + pre[r];
-        dst_row[i] = static_cast<int32_t>(row);
-        if (row >= 0 && row < m_cap) src_row[row] = static_cast<int32_t>(i);
-      } else {
-        dst_row[i] = -1;
+      for (int r = 0; r < R; ++r) {
+        const int64_t i = sub_start + kWave * r + lane;
+        if (i >= sub_end) continue;
+        const int el = key[r];
+        if (el < el_n) {
+          const int64_t row = int64_t(cnt[w * el_n + el]) + pre[r];
+          dst_row[i] = static_cast<int32_t>(row);
+          if (row >= 0 && row < m_cap) src_row[row] = static_cast<int32_t>(i);
+        } else {
+          dst_row[i] = -1;
+        }
       }
+      __syncthreads();  // cnt read out before the next pass clears it
     }
   }
 
   // padding rows of each local expert and the tail up to m_cap: -1
-  for (int el = b; el < el_n; el += gridDim.x) {
-    const int64_t hi = min(int64_t(offsets[el + 1]), m_cap);
-    for (int64_t r = int64_t(offsets[el]) + lcount[el] + threadIdx.x; r < hi; r += kThreads)
-      src_row[r] = -1;
+  for (int el = b; el < el_n; el += nt) {
+    const int64_t hi = min(int64_t(off[el + 1]), m_cap);
+    for (int64_t r = int64_t(off[el]) + total[el] + tid; r < hi; r += kThreads) src_row[r] = -1;
   }
-  for (int64_t r = int64_t(offsets[el_n]) + int64_t(b) * kThreads + threadIdx.x; r < m_cap;
-       r += int64_t(gridDim.x) * kThreads)
+  for (int64_t r = int64_t(off[el_n]) + int64_t(b) * kThreads + tid; r < m_cap;
+       r += int64_t(nt) * kThreads)
     src_row[r] = -1;
 }
 
@@ -439,8 +520,12 @@ LayoutPlan make_layout_plan(int64_t T, int E, int k, int ep, int local_rank, int
   p.e_loc = local_rank < 0 ? E : E / ep;
   p.chunk = (T / ep) * k;
   const int64_t n = T * k;
+  // about 128 tiles, 256 past 2^21 assignments (each placing workgroup reads
+  // every tile's local-expert counts; past that size, passes over its own
+  // tile cost more than those reads)
+  const int64_t target = n > (int64_t(1) << 21) ? 256 : 128;
   int tile = 1024;
-  while (tile < 8192 && int64_t(tile) * 128 < n) tile *= 2;
+  while (tile < (1 << 20) && int64_t(tile) * target < n) tile *= 2;
   p.tile = tile;
   p.tiles_per_rank = static_cast<int>((p.chunk + tile - 1) / tile);
   p.num_tiles = ep * p.tiles_per_rank;
@@ -451,9 +536,7 @@ LayoutPlan make_layout_plan(int64_t T, int E, int k, int ep, int local_rank, int
 }
 
 size_t layout_workspace_bytes(const LayoutPlan& p) {
-  return round256(sizeof(int32_t) * size_t(p.num_tiles) * p.E) +
-         round256(sizeof(int32_t) * size_t(p.num_tiles) * p.e_loc) +
-         round256(sizeof(int32_t) * size_t(p.e_loc));
+  return round256(sizeof(int32_t) * size_t(p.num_tiles) * p.E);
 }
 
 hipError_t launch_layout(const LayoutPlan& p, const int32_t* topk_idx, int32_t* expert_counts,
@@ -467,38 +550,37 @@ hipError_t launch_layout(const LayoutPlan& p, const int32_t* topk_idx, int32_t* 
                                                     offsets, dst_row, src_row, m_cap);
     return hipGetLastError();
   }
-  const Ws ws = carve(p, ws_base);
-  if (p.num_tiles > 0) {
-    layout_count_kernel<<<p.num_tiles, kThreads, sizeof(int32_t) * p.E, s>>>(p, topk_idx,
-                                                                             ws.tile_hist);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
-  }
-  const size_t scan_lds = sizeof(int32_t) * (size_t(p.ep) * p.E + p.e_loc + 16);
-  layout_scan_kernel<<<1, 1024, scan_lds, s>>>(p, ws.tile_hist, ws.tile_base, ws.lcount,
-                                               expert_counts, send_counts, split_matrix,
-                                               recv_counts, output_splits, offsets);
+  int32_t* tile_hist = static_cast<int32_t*>(ws_base);
+  layout_count_kernel<<<p.num_tiles, kThreads, sizeof(int32_t) * p.E, s>>>(p, topk_idx,
+                                                                           tile_hist);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const int grid = std::max(p.num_tiles, 1);
-  const size_t lds = sizeof(int32_t) * 8 * size_t(p.e_loc);
-  switch (p.tile / 1024) {
-    case 1:
-      layout_scatter_kernel<4><<<grid, kThreads, lds, s>>>(p, topk_idx, ws.tile_base, ws.lcount,
-                                                           offsets, dst_row, src_row, m_cap);
-      break;
-    case 2:
-      layout_scatter_kernel<8><<<grid, kThreads, lds, s>>>(p, topk_idx, ws.tile_base, ws.lcount,
-                                                           offsets, dst_row, src_row, m_cap);
-      break;
-    case 4:
-      layout_scatter_kernel<16><<<grid, kThreads, lds, s>>>(p, topk_idx, ws.tile_base, ws.lcount,
-                                                            offsets, dst_row, src_row, m_cap);
-      break;
+  // LDS of the place kernel: the per-wavefront counts (also the run sums of
+  // the offset pass, 2 x (1024 / e_loc) x e_loc <= 2048), base, offsets,
+  // totals, wave totals; the split-plan workgroup reuses it for [ep, E]
+  const size_t el = size_t(p.e_loc);
+  const size_t head = std::max(kWavesPerGroup * el, size_t(2 * (kThreads / p.e_loc)) * el);
+  const size_t words = std::max(head + 3 * el + 1 + 16, size_t(p.ep) * p.E);
+  const size_t lds = sizeof(int32_t) * words;
+  auto big_lds = [&](const void* f) {
+    if (lds > (64u << 10))
+      (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+  };
+  const int grid = p.num_tiles + 1;
+  switch (std::min(p.tile / 1024, 8)) {
+#define MOE_PLACE(RR)                                                                      \
+  case RR:                                                                                 \
+    big_lds(reinterpret_cast<const void*>(layout_place_kernel<RR>));                       \
+    layout_place_kernel<RR><<<grid, kThreads, lds, s>>>(                                   \
+        p, topk_idx, tile_hist, expert_counts, send_counts, split_matrix, recv_counts,     \
+        output_splits, offsets, dst_row, src_row, m_cap);                                  \
+    break;
+    MOE_PLACE(1)
+    MOE_PLACE(2)
+    MOE_PLACE(4)
     default:
-      layout_scatter_kernel<32><<<grid, kThreads, lds, s>>>(p, topk_idx, ws.tile_base, ws.lcount,
-                                                            offsets, dst_row, src_row, m_cap);
-      break;
+    MOE_PLACE(8)
+#undef MOE_PLACE
   }
   return hipGetLastError();
 }

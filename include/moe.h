@@ -149,8 +149,9 @@ int32_t moe_layout(const moe_layout_desc* desc, const int32_t* topk_idx_d,
  * that device current. Outputs, arguments and results are those of
  * moe_layout (the same kernels), on the current device's stream `stream`.
  * Limit: moe_layout_workspace_bytes(desc) <= MOE_LAYOUT_SCRATCH_BYTES, else
- * MOE_ERR_TOO_LARGE and nothing is launched (at 256 experts, up to about 16 M
- * assignments T * top_k). Every call on one GPU shares that GPU's array:
+ * MOE_ERR_TOO_LARGE and nothing is launched (the layout's tiles grow with the
+ * assignment count, so every layout of up to 2^30 assignments T * top_k fits,
+ * and every valid one with at most 512 experts). Every call on one GPU shares that GPU's array:
  * calls that overlap on one GPU (on two streams, or from two host threads
  * without ordering) race and must not be made. Nothing in the array needs to
  * start at zero; a call leaves its contents behind.

@@ -112,10 +112,15 @@ def test_argument_checks_return_before_launch(lib):
 
 
 def test_noalloc_layout_rejects_work_past_its_static_scratch(lib):
-    # 2^20 tokens, top-16 of 1024 experts: 2048 layout tiles of 8192 assignments,
-    # 8 MiB of per-tile histograms, past the 4 MiB static array; refused on the
-    # host, before any device call
-    T, E, k = 1 << 20, 1024, 16
+    # layout tiles grow with the assignment count (about 128 of them), so the
+    # per-tile histograms fit the 4 MiB static array up to 2^30 assignments:
+    # 2^20 tokens, top-16 of 1024 experts fits
+    d = _desc(1 << 20, 1024, 16, 1, -1, 1)
+    assert lib.moe_layout_workspace_bytes(C.byref(d)) <= 4 << 20
+    # past 2^27 the tiles stop growing: ~2^31 assignments over 1024 experts
+    # need 2048 tiles of histograms, 8 MiB, and are refused on the host, before
+    # any device call
+    T, E, k = (1 << 27) - 16, 1024, 16
     d = _desc(T, E, k, 1, -1, 1)
     assert lib.moe_layout_workspace_bytes(C.byref(d)) > 4 << 20
     m_cap = lib.moe_layout_m_cap(C.byref(d))

@@ -6,9 +6,10 @@
 One step = one pass of the whole single-GPU layer over one batch of seeded
 synthetic input already resident in HBM:
 
-    moe_route -> moe_layout -> moe_permute -> moe_grouped_gate_up -> moe_grouped_down -> moe_combine
+    moe_route -> moe_layout -> moe_grouped_gate_up_gather -> moe_grouped_down -> moe_combine
 
-The default workload is the large DeepSeek-V3-shaped layer (65536 tokens,
+(the permute fused into the gate/up GEMM's row loads; moe_permute on its own is
+timed with the calls outside the step). The default workload is the large DeepSeek-V3-shaped layer (65536 tokens,
 hidden 7168, 256 experts all local, top-8, intermediate 2048, bf16, severe
 skew), the largest that fits one GPU. Prints ONE JSON line (everything else
 goes to stderr):
@@ -220,8 +221,9 @@ def cpu_baseline(cfg, dist, layer_args, budget_s):
 
 def time_backward(args, cfg, layer, moe, stream, t_loc, n_loc, weights, x):
     """Per-call times of the calls outside the step, on this step's routing
-    and rows, after the forward timing (not part of ``value``): the forward
-    gate/up that also keeps the pre-activations, then the backward chain
+    and rows, after the forward timing (not part of ``value``): the permute on
+    its own, the forward gate/up that also keeps the pre-activations, then the
+    backward chain
     combine -> routing -> down -> gate/up (data and weight gradients) ->
     permute, each call fed by the one before it, and the per-rank
     deduplicated dispatch layout."""
@@ -253,6 +255,10 @@ def time_backward(args, cfg, layer, moe, stream, t_loc, n_loc, weights, x):
     e_act = int((L.local_counts > 0).sum().item())
     wbytes = float(e_act) * H * I * 2  # one expert matrix of each active expert
     calls = [
+        # the permute on its own (in the layer it is fused into gate/up's loads);
+        # it also fills x_perm, which the training calls below read
+        ("permute", lambda: moe.ops.permute(x, dst, layer.m_cap, out=layer.x_perm),
+         "hbm", (t_loc + n_loc) * H * 2),
         ("gate_up_save", lambda: moe.ops.grouped_gate_up_save(
             layer.x_perm, off, cnt, layer.w1t, layer.w3t, layer.h, gu), "gemm",
          (4 * nhi, 2 * wbytes + n_loc * (H + I + 2 * I) * 2)),
@@ -582,7 +588,8 @@ def main():
                    "experts": cfg.num_experts, "local_experts": len(cfg.local_experts(share)),
                    "top_k": cfg.top_k, "inter": cfg.inter, "ep_size": cfg.ep_size,
                    "local_rank": share, "align": cfg.align, "routing": dist,
-                   "local_rows": head["local_rows"], "seed": args.seed},
+                   "local_rows": head["local_rows"], "seed": args.seed,
+                   "permute": "fused into the gate/up GEMM's row loads"},
         "roofline": roof, "stages": head["stages"], "stages_cold": head.get("stages_cold"),
         "backward": backward, "extra": extra or None, "cpu_baseline": cpu,
     }

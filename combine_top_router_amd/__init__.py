@@ -9,7 +9,8 @@ with ``python -m combine_top_router_amd.build``.
 """
 from ._lib import LIB_PATH, MoEError, lib  # noqa: F401
 from .ops import (  # noqa: F401
-    Layout, alloc_layout, combine, grouped_down, grouped_gate_up, grouped_swiglu, layout,
+    Layout, alloc_layout, combine, grouped_down, grouped_gate_up, grouped_gate_up_gather,
+    grouped_swiglu, layout,
     layout_desc, layout_m_cap, layout_workspace_bytes, pack_weights, permute, route,
     validate_layout,
 )

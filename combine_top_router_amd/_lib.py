@@ -49,6 +49,8 @@ SIGNATURES = {
     "moe_combine_rows": (_I32, [_P, _I32, _I64, _P, _P, _P, _I64, _I32, _I32, _P, _P]),
     "moe_pack_weights": (_I32, [_P, _I64, _I32, _I32, _P, _P]),
     "moe_grouped_gate_up": (_I32, [_P, _P, _P, _I32, _I64, _I32, _I32, _P, _P, _P, _P]),
+    "moe_grouped_gate_up_gather": (_I32, [_P, _I64, _I32, _P, _P, _P, _I32, _I64, _I32, _I32,
+                                          _P, _P, _P, _P]),
     "moe_grouped_down": (_I32, [_P, _P, _P, _I32, _I64, _I32, _I32, _P, _P, _P]),
     "moe_grouped_swiglu": (_I32, [_P, _P, _P, _I32, _I64, _I32, _I32, _P, _P, _P, _P, _P, _P]),
     "moe_grouped_gate_up_save": (_I32, [_P, _P, _P, _I32, _I64, _I32, _I32, _P, _P, _P, _P, _P]),

@@ -56,6 +56,10 @@
 //    32-row blocks that hold rows.
 //  * Each tile's A range ends at its expert's last row: the rows past it
 //    read as zeros through the buffer bound (their results are never stored).
+//    gate/up can also gather its rows from the token rows themselves (row r
+//    of the grouped layout is token src_row[r] / top_k): each lane's A offset
+//    is then that token's row, looked up once per tile, and the expert-major
+//    copy of the activations is never written.
 //    An expert's rows are clamped to [offsets[e], m_cap), so inconsistent
 //    device counts cannot move a read or a write past the buffers.
 //  * Epilogue through LDS: fp32 -> bf16 (SwiGLU for the gated pair) into a
@@ -88,7 +92,10 @@ constexpr int kThreads = kWaves * kWave;
 //               c = [dh u silu'(g) | dh silu(g)]
 //   kKSplit     c = a [b0 | b1]^T, b0 for k < k_split and b1 past it
 //                                                           (gate/up backward)
-enum Kind { kPlain = 0, kGated = 1, kGatedSave = 2, kSwigluBwd = 3, kKSplit = 4 };
+//   kGatedGather as kGated, a holding the token rows: grouped row r is
+//               a[gather[r] / top_k]                        (gate/up with the permute fused)
+enum Kind { kPlain = 0, kGated = 1, kGatedSave = 2, kSwigluBwd = 3, kKSplit = 4,
+            kGatedGather = 5 };
 
 struct GemmArgs {
   const uint16_t* a;       // [rows, K] bf16
@@ -104,6 +111,11 @@ struct GemmArgs {
   int k_split;             // kKSplit: K index where b1 takes over
   const uint16_t* aux;     // kSwigluBwd: [rows, 2N] bf16, (g | u) of the forward
   uint16_t* aux_out;       // kGatedSave: [rows, 2N] bf16 (out)
+  // kGatedGather: a holds token rows [T, K] and grouped row r reads token
+  // gather[r] / top_k (gather = the layout's src_row)
+  const int32_t* gather;
+  int top_k;
+  uint32_t a_bytes;        // gather: bytes of a, T * K * 2 (T * K * 2 + K * 2 < 2^32)
 };
 
 __device__ __forceinline__ float silu(float g) {
@@ -158,9 +170,9 @@ __device__ __forceinline__ void with_block_count(int nb, F&& f) {
 
 template <int BM, int BN, int BK, int STAGES, int KIND, int TM>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
-  constexpr bool GATED = KIND == kGated || KIND == kGatedSave;
+  constexpr bool GATED = KIND == kGated || KIND == kGatedSave || KIND == kGatedGather;
   // the forward kinds read packed weights, the backward kinds row-major ones
-  constexpr bool BLOCKED = KIND == kGated || KIND == kGatedSave || KIND == kPlain;
+  constexpr bool BLOCKED = GATED || KIND == kPlain;
   constexpr int WROWS = 32 * TM;               // accumulator rows per wavefront
   constexpr int WAVES_M = BM / WROWS, WAVES_N = kWaves / WAVES_M;
   constexpr int OUT_N = GATED ? BN / 2 : BN;  // output columns per tile
@@ -317,17 +329,35 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
     const uint16_t* b_base0 = g.b0 + b_off;
     const uint16_t* b_base1 = (GATED || KIND == kKSplit) ? g.b1 + b_off : b_base0;
     // A's range ends at the expert's last valid row of the tile: the rows
-    // past it read as zeros (their results are never stored)
-    const i32x4 ra = make_rsrc(a_base, uint32_t(rows_valid) * uint32_t(K) * 2u);
+    // past it read as zeros (their results are never stored). With a row
+    // gather the range is all of the token rows, and a row past the tile's
+    // valid rows takes the offset a_bytes, past the range, so it reads zeros.
+    constexpr bool gathered = KIND == kGatedGather;
+    const i32x4 ra = gathered ? make_rsrc(g.a, g.a_bytes)
+                              : make_rsrc(a_base, uint32_t(rows_valid) * uint32_t(K) * 2u);
     const i32x4 rb0 = make_rsrc(b_base0, b_bytes);
     const i32x4 rb1 = make_rsrc(b_base1, b_bytes);
     // per-lane byte offsets of the first K-slice (fixed for the tile); each
     // slice adds a wave-uniform advance
     uint32_t oa[A_LOADS], ob[B_LOADS];
+    if constexpr (gathered) {
+      int src[A_LOADS];
 #pragma unroll
-    for (int i = 0; i < A_LOADS; ++i) {
-      const int r = (wid + kWaves * i) * RB + ld_r;
-      oa[i] = (uint32_t(r) * uint32_t(K) + ld_ch * 8) * 2u;
+      for (int i = 0; i < A_LOADS; ++i) {  // the row indices first, all in flight
+        const int r = (wid + kWaves * i) * RB + ld_r;
+        src[i] = r < rows_valid ? g.gather[row0 + r] : -1;
+      }
+#pragma unroll
+      for (int i = 0; i < A_LOADS; ++i)
+        oa[i] = src[i] >= 0
+                    ? (uint32_t(src[i] / g.top_k) * uint32_t(K) + ld_ch * 8) * 2u
+                    : g.a_bytes;
+    } else {
+#pragma unroll
+      for (int i = 0; i < A_LOADS; ++i) {
+        const int r = (wid + kWaves * i) * RB + ld_r;
+        oa[i] = (uint32_t(r) * uint32_t(K) + ld_ch * 8) * 2u;
+      }
     }
 #pragma unroll
     for (int i = 0; i < B_LOADS; ++i) {
@@ -484,7 +514,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
     // blocks that hold rows. A forward tile of at most 64 rows (the few rows
     // of a lightly routed expert) is bound by load latency, not by its matrix
     // work: it gets the three-stage layout
-    constexpr bool SMALL_OK = (KIND == kGated || KIND == kPlain) && TM >= 2;
+    constexpr bool SMALL_OK = (KIND == kGated || KIND == kGatedGather || KIND == kPlain) && TM >= 2;
     if (SMALL_OK && rows_valid <= 64)
       with_block_count<(TM >= 2 ? 2 : TM)>(nblk, [&](auto nb) { kloop(nb, std::bool_constant<SMALL_OK>{}); });
     else
@@ -608,6 +638,25 @@ hipError_t launch_gate_up(const void* x_perm, const int32_t* offsets, const int3
   a.c = static_cast<uint16_t*>(h);
   a.offsets = offsets, a.counts = counts, a.e_loc = e_loc, a.n = I, a.k = H, a.ldb = H;
   return launch<320, 256, 64, 2, kGated, 5>(a, s);  // I % 128 == 0: 128 output columns per tile
+}
+
+// gate/up reading its rows straight from the token rows: grouped row r is
+// x[src_row[r] / top_k] (the permute fused into the A-operand loads)
+hipError_t launch_gate_up_gather(const void* x, int64_t T, int top_k, const int32_t* src_row,
+                                 const int32_t* offsets, const int32_t* counts, int e_loc,
+                                 int64_t m_cap, int H, int I, const void* w1t, const void* w3t,
+                                 void* h, hipStream_t s) {
+  GemmArgs a{};
+  a.m_cap = m_cap;
+  a.a = static_cast<const uint16_t*>(x);
+  a.gather = src_row;
+  a.top_k = top_k;
+  a.a_bytes = static_cast<uint32_t>(T * H * 2);
+  a.b0 = static_cast<const uint16_t*>(w1t);
+  a.b1 = static_cast<const uint16_t*>(w3t);
+  a.c = static_cast<uint16_t*>(h);
+  a.offsets = offsets, a.counts = counts, a.e_loc = e_loc, a.n = I, a.k = H, a.ldb = H;
+  return launch<320, 256, 64, 2, kGatedGather, 5>(a, s);
 }
 
 hipError_t launch_gate_up_save(const void* x_perm, const int32_t* offsets, const int32_t* counts,

@@ -269,6 +269,24 @@ int32_t moe_grouped_gate_up(const void* x_perm_d, const int32_t* offsets_d,
                                        hidden, inter, w1t_d, w3t_d, h_d, as_stream(stream)));
 }
 
+int32_t moe_grouped_gate_up_gather(const void* x_d, int64_t num_tokens, int32_t top_k,
+                                   const int32_t* src_row_d, const int32_t* offsets_d,
+                                   const int32_t* counts_d, int32_t num_local_experts,
+                                   int64_t m_cap, int32_t hidden, int32_t inter,
+                                   const void* w1t_d, const void* w3t_d, void* h_d,
+                                   void* stream) {
+  const int32_t st = check_gemm(x_d, offsets_d, counts_d, num_local_experts, m_cap, hidden,
+                                inter, w1t_d, w3t_d, h_d);
+  if (st != MOE_OK) return st;
+  if (num_tokens < 0 || top_k < 1 || top_k > kMaxTopK || (m_cap > 0 && !src_row_d))
+    return MOE_ERR_ARG;
+  // the token rows are addressed with 32-bit byte offsets
+  if ((num_tokens + 1) * int64_t(hidden) * 2 >= (int64_t(1) << 32)) return MOE_ERR_UNSUPPORTED;
+  return status_of(moe::launch_gate_up_gather(x_d, num_tokens, top_k, src_row_d, offsets_d,
+                                              counts_d, num_local_experts, m_cap, hidden, inter,
+                                              w1t_d, w3t_d, h_d, as_stream(stream)));
+}
+
 int32_t moe_grouped_down(const void* h_d, const int32_t* offsets_d, const int32_t* counts_d,
                          int32_t num_local_experts, int64_t m_cap, int32_t inter, int32_t hidden,
                          const void* w2t_d, void* y_d, void* stream) {

@@ -185,6 +185,10 @@ hipError_t launch_pack(const void* w, int64_t mats, int rows, int cols, void* wt
 hipError_t launch_gate_up(const void* x_perm, const int32_t* offsets, const int32_t* counts,
                           int e_loc, int64_t m_cap, int H, int I, const void* w1t,
                           const void* w3t, void* h, hipStream_t s);
+hipError_t launch_gate_up_gather(const void* x, int64_t T, int top_k, const int32_t* src_row,
+                                 const int32_t* offsets, const int32_t* counts, int e_loc,
+                                 int64_t m_cap, int H, int I, const void* w1t, const void* w3t,
+                                 void* h, hipStream_t s);
 hipError_t launch_down(const void* h, const int32_t* offsets, const int32_t* counts, int e_loc,
                        int64_t m_cap, int I, int H, const void* w2t, void* y, hipStream_t s);
 hipError_t launch_gate_up_save(const void* x_perm, const int32_t* offsets, const int32_t* counts,

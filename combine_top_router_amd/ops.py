@@ -205,6 +205,25 @@ def grouped_gate_up(x_perm, offsets, counts, w1t, w3t, out=None):
     return out
 
 
+def grouped_gate_up_gather(x, src_row, top_k, offsets, counts, w1t, w3t, out=None):
+    """h as grouped_gate_up, its rows read straight from the token rows x [T, H]:
+    grouped row r is x[src_row[r] // top_k] (the permute fused into the GEMM's
+    loads); h has src_row's length."""
+    e_loc = _gemm_common(x, offsets, counts)
+    _need(src_row, "src_row", torch.int32)
+    T, H = x.shape
+    m_cap = src_row.numel()
+    I = w1t.shape[1]
+    _need(w1t, "w1t", torch.bfloat16, (e_loc, I, H))
+    _need(w3t, "w3t", torch.bfloat16, (e_loc, I, H))
+    out = _empty((m_cap, I), torch.bfloat16, x.device) if out is None else out
+    _need(out, "h", torch.bfloat16, (m_cap, I))
+    check("moe_grouped_gate_up_gather", lib().moe_grouped_gate_up_gather(
+        _ptr(x), T, top_k, _ptr(src_row), _ptr(offsets), _ptr(counts), e_loc, m_cap, H, I,
+        _ptr(w1t), _ptr(w3t), _ptr(out), _stream(x.device)))
+    return out
+
+
 def grouped_down(h, offsets, counts, w2t, out=None):
     """y = h W2 per local expert group; w2t is W2 [E_loc, I, H] after pack_weights
     (shape [E_loc, H, I])."""

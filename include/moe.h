@@ -272,6 +272,28 @@ int32_t moe_grouped_gate_up(const void* x_perm_d, const int32_t* offsets_d,
                             int64_t m_cap, int32_t hidden, int32_t inter,
                             const void* w1t_d, const void* w3t_d, void* h_d, void* stream);
 
+/*
+ * moe_grouped_gate_up_gather -- moe_grouped_gate_up with the permute fused
+ * into its operand loads: the rows of local expert e are read straight from
+ * the token rows, row r of the grouped layout being x[src_row[r] / top_k]
+ * (the expert-major gather of the dispatch, DeepEP issue #272: rows grouped
+ * per expert; DeepSpeed AutoEP commit text, section "Design", runtime steps
+ * 3 and 5, reorder then grouped expert compute). h is then bit-identical to
+ * moe_permute followed by moe_grouped_gate_up, and the expert-major copy of x
+ * is never written.
+ *   x_d        [T, H] bf16 token rows, 16-byte aligned
+ *   src_row_d  [m_cap] int32, moe_layout's src_row
+ *   h_d        [m_cap, I] bf16 (out); other arguments as moe_grouped_gate_up
+ * Limits as moe_grouped_gate_up, 1 <= top_k <= 16, and (T + 1) * H * 2 < 2^32
+ * (MOE_ERR_UNSUPPORTED otherwise).
+ */
+int32_t moe_grouped_gate_up_gather(const void* x_d, int64_t num_tokens, int32_t top_k,
+                                   const int32_t* src_row_d, const int32_t* offsets_d,
+                                   const int32_t* counts_d, int32_t num_local_experts,
+                                   int64_t m_cap, int32_t hidden, int32_t inter,
+                                   const void* w1t_d, const void* w3t_d, void* h_d,
+                                   void* stream);
+
 int32_t moe_grouped_down(const void* h_d, const int32_t* offsets_d, const int32_t* counts_d,
                          int32_t num_local_experts, int64_t m_cap, int32_t inter,
                          int32_t hidden, const void* w2t_d, void* y_d, void* stream);

@@ -518,3 +518,48 @@ def test_layer(name, dist, share):
     again = layer(case.x, case.logits)
     assert torch.equal(out.view(torch.int16), again.view(torch.int16))
     del layer
+
+
+# ---------------------------------------------------------------- permute fused into gate/up
+
+GATHER_CASES = [("tiny", "balanced", 1), ("ragged", "mild", 2), ("top1_odd", "balanced", -1),
+                ("tiled", "mild", 1), ("fused_edge", "severe", 3),
+                ("mixtral_8x7b", "balanced", -1), ("qwen3_30b_a3b", "zipf", -1),
+                ("deepseek_v3_ep8_share", "severe", 0), ("deepseek_v3_large", "severe", -1)]
+
+
+@pytest.mark.parametrize("name,dist,share", GATHER_CASES,
+                         ids=[f"{c}-{d}-r{s}" for c, d, s in GATHER_CASES])
+def test_gate_up_gather_equals_permute_then_gate_up(name, dist, share):
+    # the gathering gate/up reads the same operand values in the same row
+    # order as the permute followed by the plain gate/up: h bit for bit, and
+    # rows outside the expert groups untouched
+    announce("gate_up gather", name, dist, share)
+    case = get_case(name, dist, share)
+    cfg = case.cfg
+    idx, _, L = oracle_routing(case)
+    m_cap = L["m_cap"]
+    src = i32(L["src_row"])
+    off, cnt = i32(L["offsets"]), i32(L["local_counts"])
+    w1t, w3t = moe.pack_weights(case.w1), moe.pack_weights(case.w3)
+    xp = moe.permute(case.x, i32(L["dst_row"]), m_cap)
+    want = moe.grouped_gate_up(xp, off, cnt, w1t, w3t)
+    got = torch.full((m_cap, cfg.inter), 0, dtype=torch.int16, device="cuda").fill_(0x7FC1)
+    got = got.view(torch.bfloat16)
+    moe.grouped_gate_up_gather(case.x, src, cfg.top_k, off, cnt, w1t, w3t, out=got)
+    valid = torch.as_tensor(L["src_row"] >= 0, device="cuda")
+    assert torch.equal(got[valid].view(torch.int16), want[valid].view(torch.int16))
+    pad = torch.nonzero(~valid).flatten()[:4096]
+    assert (bits(got[pad]) == 0x7FC1).all()
+
+
+def test_layer_gather_equals_layer_with_permute():
+    announce("layer gather vs permute")
+    cfg = EXTRA["ragged"]
+    case = get_case("ragged", "mild", 2)
+    outs = []
+    for gather in (True, False):
+        layer = moe.MoELayer(cfg.num_tokens, cfg.hidden, cfg.num_experts, cfg.top_k, cfg.inter,
+                             case.w1, case.w3, case.w2, cfg.ep_size, 2, cfg.align, gather=gather)
+        outs.append(layer(case.x, case.logits).clone())
+    assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))

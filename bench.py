@@ -21,6 +21,8 @@ goes to stderr):
   stages       the same per stage (back to back, as inside a model)
   stages_cold  the same per stage from a cold cache: a 512 MB buffer is read and
                written before every stage, outside its events
+               (both also carry permute_alone: moe_permute timed on its own on the
+               same routing, since the step fuses the permute into gate/up)
   backward     the training and variant calls, each timed on its own
   extra        the one-GPU share of the DeepSeek-V3 EP=8 layer (balanced
                routing) as its own step, and the combine alone at the large
@@ -431,6 +433,16 @@ def run_layer(cfg, dist, args, dev, flush):
     if flush is not None:
         cold = stage_times(stages, stream, args.steps, flush)
         out["stages_cold"] = {name: roof_entry(ms, *work[name]) for name, ms in cold.items()}
+    if not any(name == "permute" for name, _ in stages):
+        # the permute is fused into gate/up in the step; time moe_permute on its
+        # own as well, on the same routing (not part of the step)
+        alone = [("permute", lambda: moe.ops.permute(x, layer.L.dst_row, layer.m_cap,
+                                                      out=layer.x_perm))]
+        ms = stage_times(alone, stream, args.steps)["permute"]
+        out["stages"]["permute_alone"] = roof_entry(ms, *work["permute"])
+        if flush is not None:
+            ms = stage_times(alone, stream, args.steps, flush)["permute"]
+            out["stages_cold"]["permute_alone"] = roof_entry(ms, *work["permute"])
     return out, (layer, x, logits, (w1, w3, w2), stream, t_loc, n_loc)
 
 

@@ -81,6 +81,12 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(WgradArgs g) {
   // each local expert's row count and first row, read once: per-tile reads
   // from memory would wait (vmcnt) for the previous tile's output stores
   __shared__ int cnt_s[kMaxExperts], off_s[kMaxExperts];
+  // local experts by descending row count (ties by index): a tile's work
+  // grows with its expert's rows while every expert has the same number of
+  // tiles, so the tiles of the largest experts go first and the short ones
+  // fill in behind them (longest first), instead of a few long tiles ending
+  // the launch alone
+  __shared__ uint16_t order_s[kMaxExperts];
 
   const int tid = threadIdx.x, lane = lane_id(), wid = uniform(tid / kWave);
   const int wm = wid / WAVES_N, wn = wid % WAVES_N;
@@ -111,6 +117,16 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(WgradArgs g) {
     off_s[e] = o;
   }
   __syncthreads();
+  for (int e = threadIdx.x; e < g.e_loc; e += kThreads) {
+    const int c = cnt_s[e];
+    int pos = 0;
+    for (int e2 = 0; e2 < g.e_loc; ++e2) {
+      const int c2 = cnt_s[e2];
+      pos += (c2 > c || (c2 == c && e2 < e)) ? 1 : 0;
+    }
+    order_s[pos] = static_cast<uint16_t>(e);
+  }
+  __syncthreads();
   const int total = g.e_loc * per_expert;
   const int G = gridDim.x;
   int slot = blockIdx.x;
@@ -125,9 +141,10 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(WgradArgs g) {
   // live in stage (kt + 1) & 1.
   bool pf = false;
   for (int tile = slot; tile < total; tile += G) {
-    const int e = tile / per_expert;
+    const int pos = tile / per_expert;
+    const int e = uniform(int(order_s[pos]));
     int mt, nt;
-    coords(tile - e * per_expert, mt, nt);
+    coords(tile - pos * per_expert, mt, nt);
     const int cnt = uniform(cnt_s[e]);
     const int64_t base = int64_t(uniform(off_s[e]));
     const int KT = (cnt + BK - 1) / BK;
@@ -254,9 +271,10 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(WgradArgs g) {
     {
       const int t2 = tile + G;
       if (t2 < total) {
-        const int e2 = t2 / per_expert;
+        const int pos2 = t2 / per_expert;
+        const int e2 = uniform(int(order_s[pos2]));
         int mt2, nt2;
-        coords(t2 - e2 * per_expert, mt2, nt2);
+        coords(t2 - pos2 * per_expert, mt2, nt2);
         const int cnt2 = uniform(cnt_s[e2]);
         if (cnt2 > 0) {
           const int64_t base2 = int64_t(uniform(off_s[e2]));

@@ -133,3 +133,20 @@ def test_noalloc_layout_rejects_work_past_its_static_scratch(lib):
                                   fake, m_cap - 1, None) == 1
     assert lib.moe_layout_noalloc(C.byref(_desc(64, 8, 2)), fake, fake, fake, fake, fake, fake,
                                   None, fake, fake, 2000, None) == 1
+
+
+def test_gate_up_gather_argument_checks_launch_nothing(lib):
+    fake = C.c_void_p(1 << 20)
+    odd = C.c_void_p((1 << 20) + 8)  # not 16-byte aligned
+    args = lambda x, T, k, src, H: (x, T, k, src, fake, fake, 4, 1024, H, 256, fake, fake,  # noqa: E731
+                                    fake, None)
+    # shapes the kernels do not implement: H not a multiple of 128; token rows
+    # past 32-bit byte offsets ((T + 1) * H * 2 >= 2^32)
+    assert lib.moe_grouped_gate_up_gather(*args(fake, 64, 2, fake, 100 * 8)) == 2
+    assert lib.moe_grouped_gate_up_gather(*args(fake, 1 << 20, 2, fake, 2048)) == 2
+    # bad arguments: misaligned x, top_k out of range, missing src_row, negative T
+    assert lib.moe_grouped_gate_up_gather(*args(odd, 64, 2, fake, 256)) == 1
+    assert lib.moe_grouped_gate_up_gather(*args(fake, 64, 0, fake, 256)) == 1
+    assert lib.moe_grouped_gate_up_gather(*args(fake, 64, 17, fake, 256)) == 1
+    assert lib.moe_grouped_gate_up_gather(*args(fake, 64, 2, None, 256)) == 1
+    assert lib.moe_grouped_gate_up_gather(*args(fake, -1, 2, fake, 256)) == 1

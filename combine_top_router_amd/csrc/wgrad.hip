@@ -75,7 +75,13 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(WgradArgs g) {
   static_assert(WAVES_M * WAVES_N == kWaves && TN >= 1 && WCOL % 32 == 0, "wavefront grid");
   static_assert(A_LOADS * 1024 * kWaves == A_BYTES && B_LOADS * 1024 * kWaves == B_BYTES,
                 "whole wave-loads");
-  static_assert(BM * WCOL * 2 <= STAGE, "an epilogue pass fits stage 0");
+  // epilogue passes: JP accumulator blocks per wavefront per pass, the most
+  // (dividing TN) whose [BM, WAVES_N * JP * 32] bf16 tile fits stage 0
+  constexpr int JP = (TN % 2 == 0 && BM * WAVES_N * (TN / 2) * 64 <= STAGE) ? TN / 2 : 1;
+  constexpr int NPASS = TN / JP, LW = WAVES_N * JP * 32, LCH = LW / 8;
+  constexpr int ST_IT = BM * LCH / kThreads;  // 16-byte chunks per thread per pass
+  static_assert(BM * LW * 2 <= STAGE && ST_IT * kThreads == BM * LCH && (LCH & (LCH - 1)) == 0,
+                "epilogue tile");
 
   __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
   // each local expert's row count and first row, read once: per-tile reads
@@ -207,12 +213,16 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(WgradArgs g) {
         fb[j] = tr_pair(sb + A_BYTES + k * (BN * 2) + off, sb + A_BYTES + (k + 4) * (BN * 2) + off);
       }
     };
+    // the products with B as the first operand: each 32x32 block of acc
+    // holds the transposed output block, so a lane's four consecutive
+    // accumulators are four consecutive output columns of one row (one
+    // packed 8-byte LDS write in the epilogue)
     auto mfma = [&](const bf16x8 (&fa)[TM], const bf16x8 (&fb)[TN]) {
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
     };
     // A step's products with slice kt2's loads between them (product q, then
     // load q): issued back to back after the barrier, every wavefront's loads
@@ -228,7 +238,7 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(WgradArgs g) {
         constexpr int q = decltype(q_tag)::value;
         if constexpr (q < NP)
           acc[q / TN][q % TN] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              fa[q / TN], fb[q % TN], acc[q / TN][q % TN], 0, 0, 0);
+              fb[q % TN], fa[q / TN], acc[q / TN][q % TN], 0, 0, 0);
         if constexpr (q < NL) {
           if (ld) load(q, ra, rb, sbase);
         }
@@ -301,32 +311,51 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(WgradArgs g) {
       }
     }
 
-    // epilogue, one pass per wavefront column: bf16 tile [BM, WCOL] in LDS,
-    // then 16-byte row stores into dW1 / dW3 (or dW2)
-    constexpr int OCH = WCOL / 8;
+    // Epilogue through a bf16 tile in stage 0, in NPASS passes. In pass p
+    // every wavefront writes its accumulator blocks j = p*JP .. p*JP + JP - 1
+    // (all eight write at once), then all threads store the tile's rows with
+    // 16-byte stores. Block (i, j) holds output row wm*64 + 32i + lane % 32
+    // and, in q, column 32j + 8(q / 4) + 4(lane / 32) + q % 4 of the
+    // wavefront's columns: four accumulators make one packed 8-byte LDS
+    // write. LDS tile column (wn*JP + jj)*32 + c holds wavefront column wn's
+    // block p*JP + jj; the 16-byte chunks of LDS row r sit XOR-swizzled by
+    // r % LCH, so the 32 rows one write touches spread over the banks.
     uint16_t* ct = reinterpret_cast<uint16_t*>(smem);
-    for (int pass = 0; pass < WAVES_N; ++pass) {
-      if (wn == pass) {
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
+    for (int pass = 0; pass < NPASS; ++pass) {
 #pragma unroll
-          for (int j = 0; j < TN; ++j)
+      for (int i = 0; i < TM; ++i) {
+        const int r = wm * 64 + i * 32 + (lane & 31);
 #pragma unroll
-            for (int q = 0; q < 16; ++q) {
-              const int r = wm * 64 + i * 32 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
-              ct[r * WCOL + j * 32 + (lane & 31)] = to_bf16(acc[i][j][q]);
-            }
+        for (int jj = 0; jj < JP; ++jj)
+#pragma unroll
+          for (int qq = 0; qq < 4; ++qq) {
+            const f32x16& a = acc[i][pass * JP + jj];
+            const int ch = (wn * JP + jj) * 4 + qq;
+            *reinterpret_cast<uint2*>(ct + r * LW + (ch ^ (r & (LCH - 1))) * 8 + 4 * (lane >> 5)) =
+                make_uint2(pack_bf16x2(a[4 * qq], a[4 * qq + 1]),
+                           pack_bf16x2(a[4 * qq + 2], a[4 * qq + 3]));
+          }
       }
       __syncthreads();
-      const int col = n0 + pass * WCOL;  // never straddles n_split (a multiple of 128)
-      const bool second = col >= g.n_split;
-      const int ld = second ? N - g.n_split : g.n_split;
-      uint16_t* dst = (second ? g.out1 : g.out0) + (int64_t(e) * M + m0) * ld +
-                      (second ? col - g.n_split : col);
-      for (int c = tid; c < BM * OCH; c += kThreads) {
-        const int r = c / OCH, ch = c % OCH;
-        *reinterpret_cast<u32x4*>(dst + int64_t(r) * ld + ch * 8) =
-            *reinterpret_cast<const u32x4*>(ct + r * WCOL + ch * 8);
+      // all of the pass's LDS reads first, then the stores
+      u32x4 v[ST_IT];
+#pragma unroll
+      for (int it = 0; it < ST_IT; ++it) {
+        const int c = tid + it * kThreads, r = c / LCH, ch = c % LCH;
+        v[it] = *reinterpret_cast<const u32x4*>(ct + r * LW + (ch ^ (r & (LCH - 1))) * 8);
+      }
+#pragma unroll
+      for (int it = 0; it < ST_IT; ++it) {
+        const int c = tid + it * kThreads, r = c / LCH, ch = c % LCH;
+        // the chunk's output column; a 32-column block never straddles n_split
+        // (a multiple of 128)
+        const int col = n0 + (ch / (4 * JP)) * WCOL + (pass * JP + (ch / 4) % JP) * 32 + (ch % 4) * 8;
+        const bool second = col >= g.n_split;
+        const int ld = second ? N - g.n_split : g.n_split;
+        uint16_t* dst = (second ? g.out1 : g.out0) + (int64_t(e) * M + m0 + r) * ld +
+                        (second ? col - g.n_split : col);
+        *reinterpret_cast<u32x4*>(dst) = v[it];
       }
       __syncthreads();  // the pass is read out before the next one (or the next tile's loads)
     }

@@ -28,6 +28,8 @@
 // both operands, sit behind the same L2. A slice's loads go out one per
 // product of the step after the barrier, not back to back; the next tile's
 // first slice is put in flight before a tile's epilogue.
+#include <mutex>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -50,6 +52,10 @@ struct WgradArgs {
   const int32_t* counts;   // [E_loc]
   int64_t m_cap;           // rows of a and b: no row at or past it is read
   int e_loc, m, n, n_split;
+  // tile queue of this launch: [0] the next dynamic tile, [1] the workgroups
+  // done; zero on entry, zero again when the last workgroup leaves. nullptr:
+  // each workgroup walks its tiles statically (tile += gridDim.x).
+  uint32_t* queue;
 };
 
 // physical 16-byte chunk of logical chunk c in slice row k (an involution)
@@ -93,6 +99,8 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(WgradArgs g) {
   // fill in behind them (longest first), instead of a few long tiles ending
   // the launch alone
   __shared__ uint16_t order_s[kMaxExperts];
+  __shared__ int next_s;  // the tile after this one (dynamic walk)
+  __shared__ long long wave_max[kWaves], wave_sum[kWaves];
 
   const int tid = threadIdx.x, lane = lane_id(), wid = uniform(tid / kWave);
   const int wm = wid / WAVES_N, wn = wid % WAVES_N;
@@ -135,6 +143,32 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(WgradArgs g) {
   __syncthreads();
   const int total = g.e_loc * per_expert;
   const int G = gridDim.x;
+  // Static walk or the queue. The queue evens out skewed experts but gives an
+  // expert's tiles to whichever workgroups free up, on any XCD, which costs
+  // L2 sharing (a few per cent under even routing), so it is taken only when
+  // the static walk's busiest workgroup would have at least 1/16 more work
+  // than the average: a tile counts its K slices plus two (its fixed cost).
+  // Every workgroup reaches the same decision from the same counts.
+  bool dyn = false;
+  if (g.queue) {
+    long long load = 0;  // the static walk's work of workgroup slot tid
+    if (tid < G)
+      for (int t = tid; t < total; t += G)
+        load += 2 + (cnt_s[order_s[t / per_expert]] + BK - 1) / BK;
+    long long mx = load, sum = load;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      mx = max(mx, __shfl_xor(mx, off, kWave));
+      sum += __shfl_xor(sum, off, kWave);
+    }
+    if (lane == 0) wave_max[wid] = mx, wave_sum[wid] = sum;
+    __syncthreads();
+    mx = 0, sum = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) mx = max(mx, wave_max[w]), sum += wave_sum[w];
+    dyn = mx * 16 * G > sum * 17;
+  }
+  uint32_t* const queue = dyn ? g.queue : nullptr;
   int slot = blockIdx.x;
   if ((G & 7) == 0) slot = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
   const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(smem));
@@ -146,7 +180,17 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(WgradArgs g) {
   // before its epilogue, which stages through stage 0 only): its slices then
   // live in stage (kt + 1) & 1.
   bool pf = false;
-  for (int tile = slot; tile < total; tile += G) {
+  // Tiles go out longest first (the experts in order_s). With the queue, after
+  // its first one a workgroup takes the next unclaimed tile whenever it
+  // finishes one: the largest experts' tiles then spread over the workgroups
+  // that free up first, instead of ending on the few workgroups a static
+  // stride gives them to (under Zipf-skewed routing the static walk left the
+  // busiest workgroups 1.2-1.6x the mean work).
+  for (int tile = slot; tile < total;) {
+    // claim the next tile now: the atomic's latency hides under the K loop,
+    // whose barriers publish next_s before anyone reads it
+    if (queue && tid == 0)
+      next_s = G + int(__hip_atomic_fetch_add(queue, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
     const int pos = tile / per_expert;
     const int e = uniform(int(order_s[pos]));
     int mt, nt;
@@ -278,8 +322,8 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(WgradArgs g) {
     // the next tile's first slice goes into stage 1 now, so its latency hides
     // under this tile's epilogue
     pf = false;
+    const int t2 = queue ? uniform(next_s) : tile + G;
     {
-      const int t2 = tile + G;
       if (t2 < total) {
         const int pos2 = t2 / per_expert;
         const int e2 = uniform(int(order_s[pos2]));
@@ -359,7 +403,53 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(WgradArgs g) {
       }
       __syncthreads();  // the pass is read out before the next one (or the next tile's loads)
     }
+    tile = t2;
   }
+  // Every workgroup, its last claim made (or none, when its first tile was
+  // already past the end), counts itself out; the last one sets the queue
+  // back to zero for the next launch on the stream. No claim can follow: each
+  // workgroup's claims returned before it counted itself out.
+  if (queue && tid == 0) {
+    if (__hip_atomic_fetch_add(queue + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+        uint32_t(G) - 1) {
+      __hip_atomic_store(queue, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(queue + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+// Tile queues: per GPU, kQueueSlots pairs of counters in a static device
+// array (zero when the library loads; each launch leaves its pair at zero).
+// A pair belongs to the first stream that uses it, so launches that may run
+// at the same time (different streams) never share one; launches on one
+// stream run one after another. Past kQueueSlots streams a launch walks its
+// tiles statically. In host code `tile_queues` is a host-side stand-in: the
+// device address of each GPU's copy comes from hipGetSymbolAddress.
+constexpr int kQueueSlots = 64;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) uint32_t tile_queues[2 * kQueueSlots];
+std::mutex queue_mu;
+uint32_t* queue_base[kMaxDevices];
+hipStream_t queue_owner[kMaxDevices][kQueueSlots];
+int queue_count[kMaxDevices];
+
+uint32_t* queue_for(hipStream_t s) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(queue_mu);
+  if (!queue_base[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(tile_queues)) != hipSuccess || !p) {
+      (void)hipGetLastError();  // the static walk needs no queue
+      return nullptr;
+    }
+    queue_base[dev] = static_cast<uint32_t*>(p);
+  }
+  for (int i = 0; i < queue_count[dev]; ++i)
+    if (queue_owner[dev][i] == s) return queue_base[dev] + 2 * i;
+  if (queue_count[dev] == kQueueSlots) return nullptr;
+  queue_owner[dev][queue_count[dev]] = s;
+  return queue_base[dev] + 2 * queue_count[dev]++;
 }
 
 template <int BM, int BN>
@@ -368,7 +458,8 @@ hipError_t launch(const WgradArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_any(const WgradArgs& a, hipStream_t s) {
+hipError_t launch_any(WgradArgs a, hipStream_t s) {
+  a.queue = queue_for(s);
   if (a.m % 256 == 0 && a.n % 256 == 0) return launch<256, 256>(a, s);
   if (a.m % 256 == 0) return launch<256, 128>(a, s);
   if (a.n % 256 == 0) return launch<128, 256>(a, s);

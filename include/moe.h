@@ -358,6 +358,15 @@ int32_t moe_grouped_gate_up_backward(const void* dgu_d, const int32_t* offsets_d
  *   dw1_d, dw3_d [E_loc, H, I] bf16 (out);  dw2_d [E_loc, I, H] bf16 (out)
  *   (the math orientation of the weights)
  * Limits as the forward calls.
+ * When the experts' row counts are skewed (a fixed tile order would give some
+ * workgroup 1/16 more work than the mean), tiles are handed out at run time
+ * from a small counter pair in library-held device memory, one pair per
+ * stream (the first 64 streams a GPU sees; later streams keep the fixed
+ * order). Each tile is one workgroup's fixed-order sum either way, so the
+ * result does not depend on the order. A launch leaves its pair at zero.
+ * Calls on different streams may overlap. A captured graph holding one of
+ * these calls uses the pair of the stream it was captured on: do not replay
+ * it while other calls run on that stream.
  */
 int32_t moe_grouped_gate_up_wgrad(const void* x_perm_d, const void* dgu_d,
                                   const int32_t* offsets_d, const int32_t* counts_d,

@@ -11,7 +11,9 @@
  *   and allocates every buffer; the library allocates nothing, keeps no state
  *   between calls and never blocks the host (moe_validate_layout excepted).
  *   The one exception to the ownership rule is moe_layout_noalloc, whose
- *   workspace is a static device array of the library (one per GPU).
+ *   workspace is a static device array of the library (one per GPU). The
+ *   weight-gradient calls also use small library-held device counters, one
+ *   pair per stream, which each call leaves at zero.
  * - `stream` is a hipStream_t (NULL = the default stream). Each call only
  *   enqueues kernels on it and returns; results are ready when the stream
  *   reaches that point. Calls on different streams may run concurrently as

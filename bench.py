@@ -253,14 +253,16 @@ def time_backward(args, cfg, layer, moe, stream, t_loc, n_loc, weights, x):
     dst, off, cnt = L.dst_row, L.offsets, L.local_counts
     dl_ep = max(cfg.ep_size, 8) if E % max(cfg.ep_size, 8) == 0 else cfg.ep_size
     sh = workloads.gen.random_rows(cfg, T, torch.bfloat16, args.seed, device=dev)
+    n_grp = int(off[-1].item())  # rows of the expert groups, padding included
     nhi = float(n_loc) * H * I
     e_act = int((L.local_counts > 0).sum().item())
     wbytes = float(e_act) * H * I * 2  # one expert matrix of each active expert
     calls = [
         # the permute on its own (in the layer it is fused into gate/up's loads);
         # it also fills x_perm, which the training calls below read
-        ("permute", lambda: moe.ops.permute(x, dst, layer.m_cap, out=layer.x_perm),
-         "hbm", (t_loc + n_loc) * H * 2),
+        ("permute", lambda: moe.ops.permute(x, dst, L.src_row, off, layer.m_cap,
+                                            out=layer.x_perm),
+         "hbm", (t_loc + n_grp) * H * 2 + n_grp * 4),
         ("gate_up_save", lambda: moe.ops.grouped_gate_up_save(
             layer.x_perm, off, cnt, layer.w1t, layer.w3t, layer.h, gu), "gemm",
          (4 * nhi, 2 * wbytes + n_loc * (H + I + 2 * I) * 2)),
@@ -332,6 +334,7 @@ def layer_work(cfg, layer):
     dst = layer.L.dst_row.cpu().numpy()
     n_loc = int(counts.sum())
     t_loc = int((dst >= 0).any(axis=1).sum())
+    n_grp = int(layer.L.offsets[-1].item())  # rows of the expert groups, padding included
     e_act = int((counts > 0).sum())
     T, H, I, E, k = cfg.num_tokens, cfg.hidden, cfg.inter, cfg.num_experts, cfg.top_k
     N = T * k
@@ -339,7 +342,8 @@ def layer_work(cfg, layer):
     work = {
         "route": ("hbm", T * E * 4 + N * 8),
         "layout": ("hbm", N * 4 * 2 + n_loc * 4),
-        "permute": ("hbm", (t_loc + n_loc) * H * 2),
+        # token rows read once, local rows written, padding rows zeroed, src_row read
+        "permute": ("hbm", (t_loc + n_grp) * H * 2 + n_grp * 4),
         "gate_up": ("gemm", (4.0 * n_loc * H * I, 2 * wbytes + n_loc * (H + I) * 2)),
         "down": ("gemm", (2.0 * n_loc * H * I, wbytes + n_loc * (I + H) * 2)),
         "combine": ("hbm", n_loc * H * 2 + N * 8 + T * H * 2),
@@ -436,7 +440,8 @@ def run_layer(cfg, dist, args, dev, flush):
     if not any(name == "permute" for name, _ in stages):
         # the permute is fused into gate/up in the step; time moe_permute on its
         # own as well, on the same routing (not part of the step)
-        alone = [("permute", lambda: moe.ops.permute(x, layer.L.dst_row, layer.m_cap,
+        alone = [("permute", lambda: moe.ops.permute(x, layer.L.dst_row, layer.L.src_row,
+                                                      layer.L.offsets, layer.m_cap,
                                                       out=layer.x_perm))]
         ms = stage_times(alone, stream, args.steps)["permute"]
         out["stages"]["permute_alone"] = roof_entry(ms, *work["permute"])

@@ -44,7 +44,7 @@ SIGNATURES = {
                                   _I64, _P]),
     "moe_dispatch_layout_workspace_bytes": (_SZ, [_I64, _I32, _I32, _I32]),
     "moe_dispatch_layout": (_I32, [_P, _I64, _I32, _I32, _I32, _P, _P, _P, _P, _P, _SZ, _P]),
-    "moe_permute": (_I32, [_P, _I64, _I32, _I32, _P, _I64, _P, _P]),
+    "moe_permute": (_I32, [_P, _I64, _I32, _I32, _P, _P, _P, _I32, _I64, _P, _P]),
     "moe_permute_weighted": (_I32, [_P, _I64, _I32, _I32, _P, _P, _I64, _P, _P]),
     "moe_combine_rows": (_I32, [_P, _I32, _I64, _P, _P, _P, _I64, _I32, _I32, _P, _P]),
     "moe_pack_weights": (_I32, [_P, _I64, _I32, _I32, _P, _P]),

@@ -84,7 +84,7 @@ const char* moe_status_string(int32_t status) {
   }
 }
 
-int32_t moe_abi_version(void) { return 1; }
+int32_t moe_abi_version(void) { return 2; }
 
 int32_t moe_route(const float* logits_d, int64_t num_tokens, int32_t num_experts, int32_t top_k,
                   int32_t* topk_idx_d, float* topk_w_d, void* stream) {
@@ -215,15 +215,17 @@ int32_t moe_dispatch_layout(const int32_t* topk_idx_d, int64_t num_tokens, int32
 }
 
 int32_t moe_permute(const void* x_d, int64_t num_tokens, int32_t hidden, int32_t top_k,
-                    const int32_t* dst_row_d, int64_t m_cap, void* x_perm_d, void* stream) {
+                    const int32_t* dst_row_d, const int32_t* src_row_d, const int32_t* offsets_d,
+                    int32_t num_local_experts, int64_t m_cap, void* x_perm_d, void* stream) {
   if (num_tokens < 0 || hidden < 8 || hidden > kMaxHidden || hidden % 8 || top_k < 1 ||
-      top_k > kMaxTopK || m_cap < 0)
+      top_k > kMaxTopK || m_cap < 0 || num_local_experts < 1 || num_local_experts > kMaxExperts)
     return MOE_ERR_ARG;
-  if (num_tokens == 0) return MOE_OK;
-  if (!x_d || !dst_row_d || !x_perm_d || !aligned16(x_d) || !aligned16(x_perm_d))
-    return MOE_ERR_ARG;
+  if (m_cap == 0) return MOE_OK;
+  if (!x_perm_d || !aligned16(x_perm_d) || !src_row_d || !offsets_d) return MOE_ERR_ARG;
+  if (num_tokens > 0 && (!x_d || !dst_row_d || !aligned16(x_d))) return MOE_ERR_ARG;
   return status_of(moe::launch_permute(x_d, num_tokens, hidden, top_k, dst_row_d, nullptr, m_cap,
-                                       x_perm_d, as_stream(stream)));
+                                       x_perm_d, src_row_d, offsets_d, num_local_experts,
+                                       as_stream(stream)));
 }
 
 int32_t moe_permute_weighted(const void* x_d, int64_t num_tokens, int32_t hidden, int32_t top_k,
@@ -236,7 +238,7 @@ int32_t moe_permute_weighted(const void* x_d, int64_t num_tokens, int32_t hidden
   if (!x_d || !dst_row_d || !topk_w_d || !x_perm_d || !aligned16(x_d) || !aligned16(x_perm_d))
     return MOE_ERR_ARG;
   return status_of(moe::launch_permute(x_d, num_tokens, hidden, top_k, dst_row_d, topk_w_d, m_cap,
-                                       x_perm_d, as_stream(stream)));
+                                       x_perm_d, nullptr, nullptr, 0, as_stream(stream)));
 }
 
 int32_t moe_pack_weights(const void* w_d, int64_t num_mats, int32_t rows, int32_t cols,

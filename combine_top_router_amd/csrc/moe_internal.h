@@ -156,8 +156,12 @@ hipError_t launch_layout(const LayoutPlan& p, const int32_t* topk_idx, int32_t* 
                          int32_t* output_splits, int32_t* offsets, int32_t* dst_row,
                          int32_t* src_row, int64_t m_cap, void* ws, hipStream_t s);
 
+// src_row, offsets and e_loc (or nullptr, nullptr, 0): also zero the padding
+// rows of the expert groups below offsets[e_loc]
 hipError_t launch_permute(const void* x, int64_t T, int H, int k, const int32_t* dst_row,
-                          const float* topk_w, int64_t m_cap, void* x_perm, hipStream_t s);
+                          const float* topk_w, int64_t m_cap, void* x_perm,
+                          const int32_t* src_row, const int32_t* offsets, int e_loc,
+                          hipStream_t s);
 hipError_t launch_combine(const void* y, int64_t y_rows, const int32_t* dst_row, const float* w,
                           int64_t T, int H, int k, void* out, hipStream_t s);
 // row_type: 0 bf16, 1 fp16, 2 fp32; w and shared may be null

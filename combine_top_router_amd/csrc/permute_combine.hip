@@ -25,15 +25,51 @@ constexpr int kTokensPerBlock = 4;  // one wavefront each
 // Each lane buffers up to kBuf vectors of its token's row before storing.
 constexpr int kBuf = 16;  // 16 x 64 lanes x 8 bf16 = 8192 elements per pass
 
+// Padding rows of the expert groups: every row r below offsets[E_loc] whose
+// src_row[r] is negative becomes zeros. The padding of a group is a run of up
+// to align - 1 rows at its end, so rows are dealt out round-robin over the
+// wavefronts doing this (row r to wavefront r mod W): each tests 64 of its
+// rows per src_row load (one ballot), then zeroes its padding rows, 1 KiB per
+// store instruction, and every run of padding spreads over as many
+// wavefronts as it has rows. Run by the permute's last `nblocks` workgroups.
+__device__ void pad_zero_rows(const int32_t* __restrict__ src_row,
+                              const int32_t* __restrict__ offsets, int e_loc, int64_t m_cap,
+                              int hv, u32x4* __restrict__ x_perm, int64_t block, int64_t nblocks) {
+  const int64_t lim = min(m_cap, static_cast<int64_t>(max(offsets[e_loc], 0)));
+  const int lane = lane_id();
+  const int64_t W = nblocks * kTokensPerBlock;
+  const int64_t w = block * kTokensPerBlock + threadIdx.x / kWave;
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+  for (int64_t j0 = 0; w + j0 * W < lim; j0 += kWave) {
+    const int64_t r = w + (j0 + lane) * W;
+    uint64_t m = __ballot(r < lim && src_row[r] < 0);
+    while (m) {
+      const int i = __builtin_ctzll(m);
+      m &= m - 1;
+      u32x4* dst = x_perm + (w + (j0 + i) * W) * hv;
+      for (int v = lane; v < hv; v += kWave) dst[v] = zero;
+    }
+  }
+}
+
 // With weights (the score applied before the experts) each copy is
-// bf16(w[t, s] * x[t]), an fp32 product rounded once.
+// bf16(w[t, s] * x[t]), an fp32 product rounded once. Workgroups from
+// tok_blocks on zero the padding rows instead (src_row given).
 template <int K, bool WEIGHTED>
 __global__ __launch_bounds__(256) void permute_kernel(const u32x4* __restrict__ x, int64_t T,
                                                       int hv, int k_rt,
                                                       const int32_t* __restrict__ dst_row,
                                                       const float* __restrict__ topk_w,
-                                                      int64_t m_cap, u32x4* __restrict__ x_perm) {
+                                                      int64_t m_cap, u32x4* __restrict__ x_perm,
+                                                      const int32_t* __restrict__ src_row,
+                                                      const int32_t* __restrict__ offsets,
+                                                      int e_loc, int64_t tok_blocks) {
 #pragma clang fp contract(off)
+  if (static_cast<int64_t>(blockIdx.x) >= tok_blocks) {
+    pad_zero_rows(src_row, offsets, e_loc, m_cap, hv, x_perm, blockIdx.x - tok_blocks,
+                  gridDim.x - tok_blocks);
+    return;
+  }
   const int k = K > 0 ? K : k_rt;
   const int64_t t = uniform(static_cast<int64_t>(blockIdx.x) * kTokensPerBlock +
                             threadIdx.x / kWave);
@@ -236,15 +272,23 @@ __global__ __launch_bounds__(256) void combine_kernel(const u32x4* __restrict__ 
 }  // namespace
 
 hipError_t launch_permute(const void* x, int64_t T, int H, int k, const int32_t* dst_row,
-                          const float* topk_w, int64_t m_cap, void* x_perm, hipStream_t s) {
-  if (T == 0) return hipSuccess;
+                          const float* topk_w, int64_t m_cap, void* x_perm,
+                          const int32_t* src_row, const int32_t* offsets, int e_loc,
+                          hipStream_t s) {
+  // one workgroup per kTokensPerBlock tokens, then (with src_row) four per CU
+  // for the padding rows
+  const int64_t tok_blocks = (T + kTokensPerBlock - 1) / kTokensPerBlock;
+  const int64_t pad_blocks = (src_row && m_cap > 0) ? 4 * device_cu_count() : 0;
+  if (tok_blocks + pad_blocks == 0) return hipSuccess;
   const int hv = H / 8;
-  const dim3 grid(static_cast<unsigned>((T + kTokensPerBlock - 1) / kTokensPerBlock));
+  const dim3 grid(static_cast<unsigned>(tok_blocks + pad_blocks));
   const u32x4* xs = static_cast<const u32x4*>(x);
   u32x4* xp = static_cast<u32x4*>(x_perm);
 #define MOE_PERMUTE(KK)                                                                          \
-  (topk_w ? permute_kernel<KK, true><<<grid, 256, 0, s>>>(xs, T, hv, k, dst_row, topk_w, m_cap, xp) \
-          : permute_kernel<KK, false><<<grid, 256, 0, s>>>(xs, T, hv, k, dst_row, topk_w, m_cap, xp))
+  (topk_w ? permute_kernel<KK, true><<<grid, 256, 0, s>>>(xs, T, hv, k, dst_row, topk_w, m_cap,  \
+                                                          xp, src_row, offsets, e_loc, tok_blocks) \
+          : permute_kernel<KK, false><<<grid, 256, 0, s>>>(xs, T, hv, k, dst_row, topk_w, m_cap, \
+                                                           xp, src_row, offsets, e_loc, tok_blocks))
   switch (k) {
     case 1: MOE_PERMUTE(1); break;
     case 2: MOE_PERMUTE(2); break;

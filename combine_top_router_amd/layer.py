@@ -59,7 +59,8 @@ class MoELayer:
                 out=self.h))]
         else:
             middle = [
-                ("permute", lambda: ops.permute(x, L.dst_row, self.m_cap, out=self.x_perm)),
+                ("permute", lambda: ops.permute(x, L.dst_row, L.src_row, L.offsets, self.m_cap,
+                                                out=self.x_perm)),
                 ("gate_up", lambda: ops.grouped_gate_up(self.x_perm, L.offsets, L.local_counts,
                                                         self.w1t, self.w3t, out=self.h)),
             ]

@@ -151,15 +151,22 @@ def validate_layout(topk_idx: torch.Tensor, L: Layout) -> None:
 
 # ---------------------------------------------------------------- permute
 
-def permute(x: torch.Tensor, dst_row: torch.Tensor, m_cap: int, out=None) -> torch.Tensor:
-    """x_perm [m_cap, H] bf16: row dst_row[t, s] holds x[t]; padding rows untouched."""
+def permute(x: torch.Tensor, dst_row: torch.Tensor, src_row: torch.Tensor,
+            offsets: torch.Tensor, m_cap: int, out=None) -> torch.Tensor:
+    """x_perm [m_cap, H] bf16: row dst_row[t, s] holds x[t]; padding rows of the
+    expert groups (src_row < 0 below offsets[E_loc]) zero; rows from
+    offsets[E_loc] on untouched."""
     _need(x, "x", torch.bfloat16)
     T, H = x.shape
     _need(dst_row, "dst_row", torch.int32)
+    _need(src_row, "src_row", torch.int32, (m_cap,))
+    _need(offsets, "offsets", torch.int32)
     k = dst_row.shape[1]
+    e_loc = offsets.numel() - 1
     out = _empty((m_cap, H), torch.bfloat16, x.device) if out is None else out
     _need(out, "x_perm", torch.bfloat16, (m_cap, H))
-    check("moe_permute", lib().moe_permute(_ptr(x), T, H, k, _ptr(dst_row), m_cap, _ptr(out),
+    check("moe_permute", lib().moe_permute(_ptr(x), T, H, k, _ptr(dst_row), _ptr(src_row),
+                                           _ptr(offsets), e_loc, m_cap, _ptr(out),
                                            _stream(x.device)))
     return out
 

@@ -202,16 +202,22 @@ int32_t moe_dispatch_layout(const int32_t* topk_idx_d, int64_t num_tokens, int32
  * text, section "Design", runtime step 3) and the local half of DeepEP's
  * dispatch (DeepEP issue #272: x, topk_idx, topk_weights in; rows grouped per
  * expert out). For every (t, slot) with dst_row[t, slot] = r >= 0:
- * x_perm[r, :] = x[t, :], a bit copy. Padding rows are not written; the
- * grouped GEMM does not read them.
- *   x_d       [T, H] bf16, 16-byte aligned
- *   dst_row_d [T, k] int32 (from moe_layout); rows >= m_cap are skipped
- *   x_perm_d  [m_cap, H] bf16 (out), 16-byte aligned
- * Limits: H a multiple of 8, 8 <= H <= 16384; 1 <= k <= 16.
+ * x_perm[r, :] = x[t, :], a bit copy (each token row read once); every row r
+ * below offsets[E_loc] with src_row[r] < 0 (the alignment padding of the
+ * expert groups) is set to zero. Rows from offsets[E_loc] to m_cap are not
+ * written.
+ *   x_d         [T, H] bf16, 16-byte aligned
+ *   dst_row_d   [T, k] int32 (from moe_layout); rows >= m_cap are skipped
+ *   src_row_d   [m_cap] int32 (from moe_layout)
+ *   offsets_d   [E_loc + 1] int32 (from moe_layout)
+ *   x_perm_d    [m_cap, H] bf16 (out), 16-byte aligned
+ * Limits: H a multiple of 8, 8 <= H <= 16384; 1 <= k <= 16;
+ * 1 <= E_loc <= 1024. T = 0 writes only the padding rows.
  */
 int32_t moe_permute(const void* x_d, int64_t num_tokens, int32_t hidden, int32_t top_k,
-                    const int32_t* dst_row_d, int64_t m_cap, void* x_perm_d,
-                    void* stream);
+                    const int32_t* dst_row_d, const int32_t* src_row_d,
+                    const int32_t* offsets_d, int32_t num_local_experts, int64_t m_cap,
+                    void* x_perm_d, void* stream);
 
 /*
  * moe_permute_weighted -- the permute with the routing score applied before
@@ -219,7 +225,8 @@ int32_t moe_permute(const void* x_d, int64_t num_tokens, int32_t hidden, int32_t
  * "Change", which the fused restore refuses): x_perm[dst_row[t, s], :] =
  * bf16(topk_w[t, s] * x[t, :]), an fp32 product rounded once. The experts
  * then see scaled rows and the restore is a plain sum (moe_combine_rows with
- * no weights). Arguments and limits as moe_permute, plus topk_w_d [T, k].
+ * no weights). x_d, dst_row_d, x_perm_d and the limits as moe_permute, plus
+ * topk_w_d [T, k]; padding rows are not written.
  */
 int32_t moe_permute_weighted(const void* x_d, int64_t num_tokens, int32_t hidden, int32_t top_k,
                              const int32_t* dst_row_d, const float* topk_w_d, int64_t m_cap,

@@ -48,7 +48,7 @@ def test_status_strings(lib):
     assert lib.moe_status_string(0) == b"MOE_OK"
     assert lib.moe_status_string(4) == b"MOE_ERR_COVERAGE"
     assert lib.moe_status_string(99) == b"MOE_ERR_UNKNOWN"
-    assert lib.moe_abi_version() == 1
+    assert lib.moe_abi_version() == 2
 
 
 def _desc(T, E, k, ep=1, lr=-1, align=128):
@@ -96,8 +96,11 @@ def test_argument_checks_return_before_launch(lib):
     assert lib.moe_layout(C.byref(d), *args, m_cap - 1, fake, ws, None) == 1   # m_cap too small
     assert lib.moe_layout(C.byref(d), *args, m_cap, fake, ws - 1, None) == 1   # workspace small
     assert lib.moe_layout(C.byref(d), *args, m_cap, odd, ws, None) == 1        # misaligned ws
-    assert lib.moe_permute(fake, 4, 12, 2, fake, 8, fake, None) == 1            # H % 8
-    assert lib.moe_permute(odd, 4, 16, 2, fake, 8, fake, None) == 1             # misaligned x
+    assert lib.moe_permute(fake, 4, 12, 2, fake, fake, fake, 2, 8, fake, None) == 1  # H % 8
+    assert lib.moe_permute(odd, 4, 16, 2, fake, fake, fake, 2, 8, fake, None) == 1   # misaligned x
+    assert lib.moe_permute(fake, 4, 16, 2, fake, None, fake, 2, 8, fake, None) == 1  # no src_row
+    assert lib.moe_permute(fake, 4, 16, 2, fake, fake, fake, 0, 8, fake, None) == 1  # E_loc = 0
+    assert lib.moe_permute(None, 0, 16, 2, None, None, None, 2, 0, None, None) == 0  # m_cap 0
     assert lib.moe_combine(fake, 8, fake, fake, 4, 16, 0, fake, None) == 1      # k = 0
     assert lib.moe_combine(fake, 8, fake, fake, 4, 16, 2, odd, None) == 1       # misaligned out
     # GEMM shapes the kernels do not implement

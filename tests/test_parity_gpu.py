@@ -220,15 +220,25 @@ def test_permute(name, dist, share):
     xp = torch.full((L["m_cap"], cfg.hidden), 0, dtype=torch.int16, device="cuda")
     xp.fill_(sentinel)
     xp = xp.view(torch.bfloat16)
-    moe.permute(case.x, i32(L["dst_row"]), L["m_cap"], out=xp)
+    moe.permute(case.x, i32(L["dst_row"]), i32(L["src_row"]), i32(L["offsets"]), L["m_cap"],
+                out=xp)
     rng = np.random.default_rng(0)
     rows = _sample_rows(L, rng) if name not in FULL else np.nonzero(L["src_row"] >= 0)[0]
     want = opermute.permute(bits(case.x), L["src_row"], cfg.top_k, rows)
     got = bits(xp[torch.as_tensor(rows, device="cuda")])
     assert (got == want).all()
-    pad = np.nonzero(L["src_row"][:L["offsets"][-1]] < 0)[0][:512]
+    # padding rows of the groups come back as zeros (the oracle's value), rows
+    # past the last group keep what they held
+    n_grp = int(L["offsets"][-1])
+    pad = np.nonzero(L["src_row"][:n_grp] < 0)[0]
     if pad.size:
-        assert (bits(xp[torch.as_tensor(pad, device="cuda")]) == sentinel).all()
+        pad = pad if name in FULL else pad[rng.choice(pad.size, min(pad.size, 4096), replace=False)]
+        want_pad = opermute.permute(bits(case.x), L["src_row"], cfg.top_k, pad)
+        assert (bits(xp[torch.as_tensor(pad, device="cuda")]) == want_pad).all()
+        assert not want_pad.any()
+    tail = np.arange(n_grp, min(L["m_cap"], n_grp + 512))
+    if tail.size:
+        assert (bits(xp[torch.as_tensor(tail, device="cuda")]) == sentinel).all()
 
 
 # ---------------------------------------------------------------- grouped SwiGLU
@@ -542,7 +552,7 @@ def test_gate_up_gather_equals_permute_then_gate_up(name, dist, share):
     src = i32(L["src_row"])
     off, cnt = i32(L["offsets"]), i32(L["local_counts"])
     w1t, w3t = moe.pack_weights(case.w1), moe.pack_weights(case.w3)
-    xp = moe.permute(case.x, i32(L["dst_row"]), m_cap)
+    xp = moe.permute(case.x, i32(L["dst_row"]), src, off, m_cap)
     want = moe.grouped_gate_up(xp, off, cnt, w1t, w3t)
     got = torch.full((m_cap, cfg.inter), 0, dtype=torch.int16, device="cuda").fill_(0x7FC1)
     got = got.view(torch.bfloat16)

@@ -241,6 +241,29 @@ def test_permute(name, dist, share):
         assert (bits(xp[torch.as_tensor(tail, device="cuda")]) == sentinel).all()
 
 
+def test_permute_padding_without_tokens():
+    """No token rows to copy, only padding: groups given by hand (three
+    experts, 5, 0 and 3 rows padded to 8) with src_row -1 on the padding rows
+    and on two rows no token fills; those rows come back zero, the rest of
+    x_perm keeps its sentinel."""
+    announce("permute padding only")
+    H, k, m_cap = 136, 2, 40
+    offsets = np.array([0, 8, 8, 16], np.int32)
+    src = np.full(m_cap, -1, np.int32)
+    src[[0, 1, 2, 3, 4, 8, 9, 10]] = [0, 1, 2, 3, 4, 5, 6, 7]  # rows the tokens would fill
+    sentinel = 0x7FC1
+    xp = torch.full((m_cap, H), sentinel, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    x = torch.zeros((1, H), dtype=torch.bfloat16, device="cuda")
+    dst = torch.zeros((0, k), dtype=torch.int32, device="cuda")
+    moe.permute(x[:0], dst, i32(src), i32(offsets), m_cap, out=xp)
+    got = bits(xp)
+    pad = [r for r in range(offsets[-1]) if src[r] < 0]
+    assert pad == [5, 6, 7, 11, 12, 13, 14, 15]
+    assert (got[pad] == 0).all()
+    keep = [r for r in range(m_cap) if r not in pad]
+    assert (got[keep] == sentinel).all()
+
+
 # ---------------------------------------------------------------- grouped SwiGLU
 
 WINDOW = 80  # rows: every 160-row half of a row tile holds two whole windows

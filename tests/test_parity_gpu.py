@@ -182,6 +182,25 @@ def test_layout_all_to_one_expert():
         assert (getattr(L, key).cpu().numpy() == want[key]).all(), key
 
 
+@pytest.mark.parametrize("T,ep,share", [(1 << 19, 1, -1), (1 << 21, 8, 3)])
+def test_layout_tiles_walked_in_several_passes(T, ep, share):
+    """4 M and 16 M assignments (top-8 of 256 experts): tiles of 16384 and 65536
+    assignments, each placed in several passes with every expert's next row
+    carried from pass to pass. Distinct ids per token, skewed toward low
+    experts (43 of the 256 get nothing)."""
+    announce("layout multi-pass", T, ep, share)
+    k, E = 8, 256
+    rng = np.random.default_rng(7)
+    first = (rng.pareto(1.5, T) * 20).astype(np.int64) % (3 * E // 4)
+    idx = ((first[:, None] + np.arange(k)[None, :] * 3) % E).astype(np.int32)
+    want = olayout.layout(idx, E, ep, share, 128)
+    L = moe.layout(i32(idx), E, ep, share, 128)
+    assert L.m_cap == want["m_cap"]
+    for key in LAYOUT_KEYS:
+        got = getattr(L, key).cpu().numpy()
+        assert (got == want[key]).all(), (key, np.argwhere(got != want[key])[:5])
+
+
 def test_validator_reports_bad_input():
     announce("validator")
     idx = np.array([[0, 1], [1, 2], [2, 3], [3, 0]], np.int32)
